@@ -1,0 +1,146 @@
+"""Double-precision CPU attention oracle (ctypes binding of attn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The GPU library never imports, links
+or executes anything in this directory, and this directory never imports the
+GPU library.
+
+The oracle evaluates exact attention row by row in double precision with the
+row maximum subtracted before the exponential, as the double-precision CPU
+reference of the page "attention.cu" does, with the causal mask and the
+log-sum-exp output of "Flash attention in PyTorch, then in Triton" (sections
+"Attention by hand" and "Backwards, and training with it"). The log-sum-exp
+is returned in natural-log units.
+
+Parity pins live in tests/test_oracle_pins.py; every function here has one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+# The mutation test of the pins points this at deliberately broken builds of
+# a copy of the source; everything else uses the in-tree library.
+LIBRARY = os.environ.get("ATTN_ORACLE_LIBRARY",
+                         os.path.join(_HERE, "liboracle.so"))
+
+# -O2, no fast-math, no floating-point contraction: every product and sum is
+# a separately rounded double operation.
+CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+          "-ffp-contract=off", "-fno-fast-math"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile attn_oracle.c into liboracle.so with gcc; returns the path."""
+    if not force and os.path.exists(LIBRARY) and \
+            os.path.getmtime(LIBRARY) >= os.path.getmtime(SOURCE):
+        return LIBRARY
+    tmp = LIBRARY + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, "-o", tmp, SOURCE, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                build()
+            lib = ctypes.CDLL(LIBRARY)
+            f = lib.oracle_attention
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 4 + [
+                ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int]
+            g = lib.oracle_probabilities
+            g.restype = ctypes.c_int
+            g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                          ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                          ctypes.c_void_p]
+            lib.oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle uses by default on this host."""
+    return int(_load().oracle_max_threads())
+
+
+def _as_f32(x) -> np.ndarray:
+    """Widen to a C-contiguous float32 numpy array (exact for bf16/fp16)."""
+    try:  # torch tensors are accepted too (CPU, any float dtype)
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        x = x.astype(np.float32)
+    return np.ascontiguousarray(x)
+
+
+def attention(q, k, v, causal: bool, scale: float, rows=None,
+              threads: int = 0):
+    """Exact attention in double precision.
+
+    q, k, v: [B, H, T, D] (or [T, D] for one head), float32 or exactly
+    widenable to it. rows: optional 1-D int array of flat row ids
+    (b * H + h) * T + t. Returns (o, lse) as float64: o is [B, H, T, D]
+    (or [len(rows), D]), lse is [B, H, T] (or [len(rows)]).
+    """
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    single = q.ndim == 2
+    if single:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, T, D] shape")
+    B, H, T, D = q.shape
+    if rows is not None:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows.shape[0]
+        o = np.empty((n, D), np.float64)
+        lse = np.empty((n,), np.float64)
+        rptr = rows.ctypes.data
+    else:
+        n = B * H * T
+        o = np.empty((B, H, T, D), np.float64)
+        lse = np.empty((B, H, T), np.float64)
+        rptr = None
+    rc = _load().oracle_attention(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, T, D,
+        int(bool(causal)), float(scale), rptr, n, o.ctypes.data,
+        lse.ctypes.data, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_attention failed (%d)" % rc)
+    if single and rows is None:
+        return o[0, 0], lse[0, 0]
+    return o, lse
+
+
+def probabilities(q, k, causal: bool, scale: float) -> np.ndarray:
+    """Full [T, T] softmax-weight table of one head (q, k: [T, D])."""
+    q, k = _as_f32(q), _as_f32(k)
+    if q.ndim != 2 or q.shape != k.shape:
+        raise ValueError("q, k must share one [T, D] shape")
+    T, D = q.shape
+    P = np.empty((T, T), np.float64)
+    rc = _load().oracle_probabilities(q.ctypes.data, k.ctypes.data, T, D,
+                                      int(bool(causal)), float(scale),
+                                      P.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_probabilities failed (%d)" % rc)
+    return P

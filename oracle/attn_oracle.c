@@ -1,0 +1,191 @@
+/*
+ * Attention oracle: a plain, slow, double-precision CPU evaluation of exact
+ * scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file or the library built from it; only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark use it. It shares no
+ * source, header, helper or constant with the GPU library.
+ *
+ * What it computes, per query row i of one (batch, head) slice:
+ *
+ *   visible keys J_i = {0 .. T-1}, or {0 .. i} when causal
+ *       (causal mask: a token sees the tokens up to and including its own;
+ *        "Flash attention in PyTorch, then in Triton", section "Attention's
+ *        table of scores" and "Attention by hand")
+ *   s_j   = scale * sum_e q[i,e] * k[j,e]                   for j in J_i
+ *   m     = max_j s_j
+ *   w_j   = exp(s_j - m),  Z = sum_j w_j                    (safe softmax)
+ *   O[i,e] = (sum_j w_j * v[j,e]) / Z
+ *   lse_i = m + log Z           (natural-log log-sum-exp of the scaled,
+ *                                masked scores)
+ *
+ * The row-at-a-time, max-subtracted evaluation in double with one row of
+ * scratch follows the double-precision CPU reference of the page
+ * "attention.cu" (its attentionCpu function); the causal mask and the
+ * log-sum-exp side output follow "Flash attention in PyTorch, then in
+ * Triton" (sections "Attention by hand" and "Backwards, and training with
+ * it"). The log-sum-exp is reported in natural-log units; that page keeps it
+ * in base-2 units inside its kernel, which is the same quantity times log2(e).
+ *
+ * Inputs are float32 arrays (bf16/fp16 inputs are passed already widened to
+ * float32, which is exact); every product and sum is done in double. There is
+ * no blocking, no fusion and no reordering of the arithmetic: for every output
+ * element the sums run over j (or e) in ascending order. Build without
+ * fast-math and without floating-point contraction.
+ *
+ * Parity pins (each checked by the test suite against closed forms, library
+ * routines or brute force, never against this file itself):
+ *   T = 1 returns V; Q = 0 returns the (prefix) mean of V; one-hot scores
+ *   select one V row; probability rows sum to 1; brute force on tiny shapes;
+ *   float64 scaled_dot_product_attention on small shapes; key-shift,
+ *   V-affine, causal-prefix, slice-independence and permutation invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One query row of one (batch, head) slice. q_row: D floats; k, v: T x D
+ * floats of that slice; scratch: at least T doubles; o_row: D doubles. */
+static void oracle_one_row(const float* q_row, const float* k, const float* v,
+                           int64_t T, int64_t D, int causal, double scale,
+                           int64_t i, double* scratch, double* o_row,
+                           double* lse_out) {
+    const int64_t visible = causal ? (i + 1) : T;
+
+    /* scores and their maximum */
+    double best = -INFINITY;
+    for (int64_t j = 0; j < visible; ++j) {
+        double dot = 0.0;
+        for (int64_t e = 0; e < D; ++e) {
+            dot += (double)q_row[e] * (double)k[j * D + e];
+        }
+        const double s = scale * dot;
+        scratch[j] = s;
+        if (s > best) best = s;
+    }
+
+    /* exponentials with the maximum subtracted, and their sum */
+    double total = 0.0;
+    for (int64_t j = 0; j < visible; ++j) {
+        const double w = exp(scratch[j] - best);
+        scratch[j] = w;
+        total += w;
+    }
+
+    /* weighted sum of the values; for each e the sum runs over j ascending */
+    for (int64_t e = 0; e < D; ++e) o_row[e] = 0.0;
+    for (int64_t j = 0; j < visible; ++j) {
+        const double w = scratch[j];
+        const float* vj = v + j * D;
+        for (int64_t e = 0; e < D; ++e) {
+            o_row[e] += w * (double)vj[e];
+        }
+    }
+    for (int64_t e = 0; e < D; ++e) o_row[e] /= total;
+
+    if (lse_out) *lse_out = best + log(total);
+}
+
+/*
+ * Attention for a set of query rows.
+ *
+ * q, k, v : float32, contiguous [B, H, T, D].
+ * rows    : flat row ids (b * H + h) * T + t, or NULL for every row in order.
+ * nrows   : number of entries of `rows` (ignored when rows is NULL).
+ * o       : double [nrows, D] (or [B*H*T, D] when rows is NULL).
+ * lse     : double [nrows] or NULL.
+ * nthreads: OpenMP threads (<= 0: the runtime default).
+ *
+ * Returns 0, or -1 on invalid arguments (nothing written).
+ */
+int oracle_attention(const float* q, const float* k, const float* v,
+                     int64_t B, int64_t H, int64_t T, int64_t D, int causal,
+                     double scale, const int64_t* rows, int64_t nrows,
+                     double* o, double* lse, int nthreads) {
+    if (!q || !k || !v || !o || B < 1 || H < 1 || T < 1 || D < 1) return -1;
+    const int64_t all = B * H * T;
+    const int64_t n = rows ? nrows : all;
+    if (n < 0) return -1;
+    if (rows) {
+        for (int64_t r = 0; r < n; ++r) {
+            if (rows[r] < 0 || rows[r] >= all) return -1;
+        }
+    }
+    int bad = 0;
+
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double* scratch = (double*)malloc((size_t)T * sizeof(double));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            bad = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t r = 0; r < n; ++r) {
+            if (!scratch) continue;
+            const int64_t flat = rows ? rows[r] : r;
+            const int64_t slice = flat / T;
+            const int64_t t = flat % T;
+            const float* qs = q + slice * T * D;
+            const float* ks = k + slice * T * D;
+            const float* vs = v + slice * T * D;
+            oracle_one_row(qs + t * D, ks, vs, T, D, causal, scale, t,
+                           scratch, o + r * D, lse ? lse + r : NULL);
+        }
+        free(scratch);
+    }
+    (void)nthreads;
+    return bad ? -2 : 0;
+}
+
+/*
+ * The full probability table of one head, for tiny shapes: P[i, j] is the
+ * softmax weight of key j for query i (0 for a masked key). q, k: float32
+ * [T, D]; P: double [T, T]. Same arithmetic as oracle_one_row.
+ */
+int oracle_probabilities(const float* q, const float* k, int64_t T, int64_t D,
+                         int causal, double scale, double* P) {
+    if (!q || !k || !P || T < 1 || D < 1) return -1;
+    for (int64_t i = 0; i < T; ++i) {
+        const int64_t visible = causal ? (i + 1) : T;
+        double* row = P + i * T;
+        double best = -INFINITY;
+        for (int64_t j = 0; j < visible; ++j) {
+            double dot = 0.0;
+            for (int64_t e = 0; e < D; ++e) {
+                dot += (double)q[i * D + e] * (double)k[j * D + e];
+            }
+            row[j] = scale * dot;
+            if (row[j] > best) best = row[j];
+        }
+        double total = 0.0;
+        for (int64_t j = 0; j < visible; ++j) {
+            row[j] = exp(row[j] - best);
+            total += row[j];
+        }
+        for (int64_t j = 0; j < visible; ++j) row[j] /= total;
+        for (int64_t j = visible; j < T; ++j) row[j] = 0.0;
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use by default. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,60 @@
+"""The oracle's pins must catch plausible mistakes. Each case below plants one
+mistake in a copy of the oracle's C source (on the CPU, in a temporary
+directory), builds it, and runs the pin suite against that build: at least one
+pin must fail. The in-tree oracle is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, [(text in the source, planted replacement), ...])
+MUTANTS = [
+    ("no_max_subtraction", [("exp(scratch[j] - best)", "exp(scratch[j])"),
+                            ("exp(row[j] - best)", "exp(row[j])"),
+                            ("best + log(total)", "log(total)")]),
+    ("causal_excludes_diagonal", [("causal ? (i + 1) : T", "causal ? i : T")]),
+    ("causal_one_too_many", [("causal ? (i + 1) : T",
+                              "causal ? (i + 2 < T ? i + 2 : T) : T")]),
+    ("key_operand_transposed", [("(double)k[j * D + e]", "(double)k[e * T + j]")]),
+    ("scale_dropped", [("const double s = scale * dot;", "const double s = dot;"),
+                       ("row[j] = scale * dot;", "row[j] = dot;")]),
+    ("scale_applied_twice", [("const double s = scale * dot;",
+                              "const double s = scale * scale * dot;")]),
+    ("lse_base_two", [("best + log(total)", "best + log2(total)")]),
+    ("no_normalisation", [("o_row[e] /= total;", "o_row[e] /= 1.0;"),
+                          ("row[j] /= total;", "row[j] /= 1.0;")]),
+    ("value_row_fixed", [("v + j * D;", "v;")]),
+    ("value_weight_sign", [("o_row[e] += w * (double)vj[e];",
+                            "o_row[e] -= w * (double)vj[e];")]),
+    ("sum_drops_first_key", [("for (int64_t j = 0; j < visible; ++j) {\n"
+                              "        const double w = exp(",
+                              "for (int64_t j = 0; j < visible; ++j) {\n"
+                              "        if (j == 0) { scratch[j] = 0; continue; }\n"
+                              "        const double w = exp(")]),
+]
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, edits, tmp_path):
+    src = open(oracle.SOURCE).read()
+    for old, new in edits:
+        assert old in src, f"mutation site {old!r} not found"
+        src = src.replace(old, new)
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(src)
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", str(lib), str(csrc), "-lm"],
+                   check=True)
+    env = dict(os.environ, ATTN_ORACLE_LIBRARY=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q",
+                        "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]

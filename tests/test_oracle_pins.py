@@ -1,0 +1,290 @@
+"""Pins of the double-precision oracle against things other than itself:
+closed forms, a hand-computable example, brute force, a library routine and
+invariants of the mathematics. These run on the CPU.
+
+What the oracle computes is the plain definition of causal/non-causal scaled
+dot-product attention ("Flash attention in PyTorch, then in Triton", section
+"Attention by hand"), evaluated with the maximum subtracted as in the
+double-precision CPU reference of the page "attention.cu".
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_amd.inputs import make_qkv, late_spike_qkv
+
+D = 64
+
+
+def rand(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.standard_normal(shape).astype(np.float32)
+
+
+# --- closed forms -----------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token_returns_v(causal):
+    """T = 1: the one weight is exp(0) / exp(0) = 1, so O = V exactly and the
+    log-sum-exp is the single scaled score."""
+    q, k, v = (rand((2, 3, 1, D), s) for s in (1, 2, 3))
+    scale = 0.125
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    assert np.array_equal(o, v.astype(np.float64))
+    for b in range(2):
+        for h in range(3):
+            want = scale * math.fsum(float(a) * float(c)
+                                     for a, c in zip(q[b, h, 0], k[b, h, 0]))
+            assert lse[b, h, 0] == pytest.approx(want, rel=1e-14, abs=1e-15)
+
+
+@pytest.mark.parametrize("T", [1, 7, 100, 257])
+def test_zero_query_gives_prefix_mean(T):
+    """Q = 0: every visible key scores 0, the weights are uniform, O_i is the
+    mean of the visible V rows and lse_i = log(#visible)."""
+    _, k, v = (rand((1, 2, T, D), s) for s in (4, 5, 6))
+    q = np.zeros_like(k)
+    o, lse = oracle.attention(q, k, v, True, 0.125)
+    v64 = v.astype(np.float64)
+    counts = np.arange(1, T + 1, dtype=np.float64)
+    prefix_mean = np.cumsum(v64, axis=2) / counts[None, None, :, None]
+    np.testing.assert_allclose(o, prefix_mean, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(counts), lse.shape),
+                               rtol=0, atol=1e-15)
+    o, lse = oracle.attention(q, k, v, False, 0.125)
+    np.testing.assert_allclose(o, np.broadcast_to(v64.mean(axis=2, keepdims=True),
+                                                  o.shape), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(T), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_hot_scores_select_one_value_row(causal):
+    """Key j is the basis vector e_j and query i is alpha * e_pi(i): query i
+    scores alpha*scale on key pi(i) and 0 on every other key. With a gap of
+    1000 the other weights underflow to exactly 0 in double, so O_i = V_pi(i)
+    exactly and lse_i = alpha * scale."""
+    T = 48
+    g = np.random.Generator(np.random.PCG64(7))
+    pi = np.array([g.integers(0, i + 1) if causal else g.integers(0, T)
+                   for i in range(T)])
+    alpha, scale = 8000.0, 0.125
+    k = np.zeros((T, D), np.float32)
+    k[np.arange(T), np.arange(T)] = 1.0
+    q = np.zeros((T, D), np.float32)
+    q[np.arange(T), pi] = alpha
+    v = rand((T, D), 8)
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    assert np.array_equal(o, v[pi].astype(np.float64))
+    assert np.all(lse == alpha * scale)
+
+
+def test_two_keys_hand_computed():
+    """A worked two-key example: q = (a, 0, ...), k_j = (b_j, 0, ...), so the
+    scores are s_j = scale * a * b_j and O = sigmoid-weighted average of the
+    two V rows, written out by hand. Scores near 1000 make a softmax without
+    the maximum subtracted overflow, so this also pins the subtraction."""
+    a, scale = 40.0, 0.125
+    for b0, b1 in [(200.0, 199.75), (-3.0, 5.0), (1.0, 1.0)]:
+        q = np.zeros((2, D), np.float32)
+        k = np.zeros((2, D), np.float32)
+        q[:, 0] = a
+        k[0, 0], k[1, 0] = b0, b1
+        v = rand((2, D), 9)
+        o, lse = oracle.attention(q, k, v, False, scale)
+        s0, s1 = scale * a * b0, scale * a * b1
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))  # weight of key 1
+        want = (1.0 - w1) * v[0].astype(np.float64) + w1 * v[1].astype(np.float64)
+        np.testing.assert_allclose(o[0], want, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(o[1], want, rtol=0, atol=1e-13)
+        top = max(s0, s1)
+        want_lse = top + math.log1p(math.exp(min(s0, s1) - top))
+        assert lse[0] == pytest.approx(want_lse, rel=1e-15)
+        # causal: row 0 sees key 0 only
+        o, lse = oracle.attention(q, k, v, True, scale)
+        assert np.array_equal(o[0], v[0].astype(np.float64))
+        assert lse[0] == s0
+        np.testing.assert_allclose(o[1], want, rtol=0, atol=1e-13)
+
+
+# --- probabilities ----------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    T = 50
+    q, k, v = (rand((T, D), s) for s in (10, 11, 12))
+    P = oracle.probabilities(q, k, causal, 0.125)
+    assert np.all(P >= 0)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=0, atol=T * 2.0 ** -52)
+    if causal:
+        assert np.all(P[np.triu_indices(T, 1)] == 0.0)
+        assert np.all(np.diag(P) > 0)
+    # the table weighs V into the same output the row evaluator produces
+    o, _ = oracle.attention(q, k, v, causal, 0.125)
+    np.testing.assert_allclose(P @ v.astype(np.float64), o, rtol=0, atol=1e-13)
+
+
+# --- brute force --------------------------------------------------------------
+
+def brute_force(q, k, v, causal, scale):
+    """Textbook softmax in long double, with no maximum subtracted (safe at
+    these magnitudes), the full score table built at once."""
+    ld = np.longdouble
+    q, k, v = q.astype(ld), k.astype(ld), v.astype(ld)
+    T = q.shape[0]
+    S = ld(scale) * (q @ k.T)
+    W = np.exp(S)
+    if causal:
+        W = np.where(np.tril(np.ones((T, T), bool)), W, ld(0))
+    Z = W.sum(axis=1, keepdims=True)
+    return (W / Z) @ v, np.log(Z[:, 0])
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 13, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(T, causal):
+    for seed in range(3):
+        q, k, v = (rand((T, D), 100 * seed + s) for s in (1, 2, 3))
+        scale = [0.125, 0.3, 1.0][seed]
+        o, lse = oracle.attention(q, k, v, causal, scale)
+        bo, blse = brute_force(q, k, v, causal, scale)
+        np.testing.assert_allclose(o, bo.astype(np.float64), rtol=0, atol=2e-14)
+        np.testing.assert_allclose(lse, blse.astype(np.float64), rtol=0,
+                                   atol=2e-14)
+
+
+# --- library routine ------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 100, 256, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_float64(T, causal):
+    """torch's scaled_dot_product_attention in float64 on the CPU, on the test
+    shapes of "Flash attention in PyTorch, then in Triton" (two sequences of
+    three heads), and torch.logsumexp for the log-sum-exp."""
+    q, k, v = make_qkv(2, 3, T, D, "f32", 1100 + T)
+    scale = 0.125
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    q64, k64, v64 = (x.double() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q64, k64, v64, is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = scale * (q64 @ k64.transpose(-1, -2).contiguous())
+    if causal:
+        s = s.masked_fill(~torch.ones(T, T, dtype=torch.bool).tril(), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(),
+                               rtol=0, atol=1e-12)
+
+
+# --- invariants -----------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift(causal):
+    """Adding one vector u to every key shifts row i's scores by scale*q_i.u:
+    O is unchanged and lse_i moves by that amount. The shift here is large
+    (|scale*q.u| well past 709), so an evaluator that skipped the maximum
+    subtraction would overflow a double."""
+    T = 120
+    q, k, v = (rand((1, 1, T, D), s) for s in (21, 22, 23))
+    # keys on a 2^-10 grid, so k + u (|u| <= 1024) is exact in float32
+    k = np.round(k * 1024).astype(np.float32) / np.float32(1024)
+    scale = 0.125
+    u = np.zeros(D, np.float32)
+    u[:4] = [2048.0, -2048.0, 2048.0, 2048.0]
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    o2, lse2 = oracle.attention(q, k + u, v, causal, scale)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-9)
+    shift = scale * (q.astype(np.float64)[..., :] @ u.astype(np.float64))
+    np.testing.assert_allclose(lse2 - lse, shift, rtol=1e-12, atol=1e-9)
+    assert np.abs(shift).max() > 709
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_affine(causal):
+    """The weights sum to 1: O(a*V + b) = a*O(V) + b."""
+    T = 77
+    q, k, v = (rand((1, 2, T, D), s) for s in (31, 32, 33))
+    # v and b on a 2^-10 grid, so a*v + b is exact in float32
+    v = np.round(v * 1024).astype(np.float32) / np.float32(1024)
+    a = np.float32(-2.5)
+    b = np.round(rand((D,), 34) * 1024).astype(np.float32) / np.float32(1024)
+    o, _ = oracle.attention(q, k, v, causal, 0.125)
+    o2, _ = oracle.attention(q, k, a * v + b, causal, 0.125)
+    want = float(a) * o + b.astype(np.float64)
+    np.testing.assert_allclose(o2, want, rtol=0, atol=1e-12)
+
+
+def test_causal_prefix_only():
+    """Causal row i depends on rows <= i of K and V only."""
+    T = 64
+    q, k, v = (rand((1, 1, T, D), s) for s in (41, 42, 43))
+    o, lse = oracle.attention(q, k, v, True, 0.125)
+    i = 29
+    k2, v2 = k.copy(), v.copy()
+    k2[..., i + 1:, :] = rand(k2[..., i + 1:, :].shape, 44) * 50
+    v2[..., i + 1:, :] = rand(v2[..., i + 1:, :].shape, 45) * 50
+    o2, lse2 = oracle.attention(q, k2, v2, True, 0.125)
+    assert np.array_equal(o2[..., : i + 1, :], o[..., : i + 1, :])
+    assert np.array_equal(lse2[..., : i + 1], lse[..., : i + 1])
+    assert not np.allclose(o2[..., i + 1:, :], o[..., i + 1:, :])
+
+
+def test_slices_independent_and_row_subsets():
+    q, k, v = make_qkv(2, 3, 40, D, "f32", 77)
+    qn, kn, vn = (x.numpy() for x in (q, k, v))
+    o, lse = oracle.attention(qn, kn, vn, True, 0.125)
+    for b in range(2):
+        for h in range(3):
+            o1, l1 = oracle.attention(qn[b, h], kn[b, h], vn[b, h], True, 0.125)
+            assert np.array_equal(o1, o[b, h]) and np.array_equal(l1, lse[b, h])
+    rows = np.array([0, 5, 39, 40, 41, 150, 239])
+    orow, lrow = oracle.attention(qn, kn, vn, True, 0.125, rows=rows)
+    assert np.array_equal(orow, o.reshape(-1, D)[rows])
+    assert np.array_equal(lrow, lse.reshape(-1)[rows])
+
+
+def test_noncausal_permutation_invariant():
+    T = 90
+    q, k, v = (rand((T, D), s) for s in (51, 52, 53))
+    perm = np.random.Generator(np.random.PCG64(54)).permutation(T)
+    o, lse = oracle.attention(q, k, v, False, 0.125)
+    o2, lse2 = oracle.attention(q, k[perm], v[perm], False, 0.125)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+
+
+def test_negative_and_zero_scale():
+    """scale = 0 gives uniform weights (the prefix mean); a negative scale is
+    the same as negating the queries."""
+    T = 33
+    q, k, v = (rand((T, D), s) for s in (61, 62, 63))
+    o, lse = oracle.attention(q, k, v, True, 0.0)
+    counts = np.arange(1, T + 1, dtype=np.float64)
+    np.testing.assert_allclose(o, np.cumsum(v.astype(np.float64), 0) /
+                               counts[:, None], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(counts), rtol=0, atol=1e-15)
+    o1, l1 = oracle.attention(q, k, v, True, -0.2)
+    o2, l2 = oracle.attention(-q, k, v, True, 0.2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_late_spike_moves_max_in_last_tile():
+    """The stress input: the amplified late key is the row maximum of most
+    rows, i.e. the running maximum still moves in the last 64-key tile."""
+    q, k, v = late_spike_qkv(256)
+    qn, kn = q.numpy()[0, 0].astype(np.float64), k.numpy()[0, 0].astype(np.float64)
+    s = 0.125 * qn @ kn.T
+    assert (np.argmax(s, axis=1) >= 192).mean() > 0.3
+    o, _ = oracle.attention(q, k, v, False, 0.125)
+    bo, _ = brute_force(q.numpy()[0, 0], k.numpy()[0, 0], v.numpy()[0, 0],
+                        False, 0.125)
+    np.testing.assert_allclose(o[0, 0], bo.astype(np.float64), rtol=0, atol=1e-13)
+
+
+def test_invalid_arguments_rejected():
+    q = np.zeros((1, 1, 4, D), np.float32)
+    with pytest.raises(ValueError):
+        oracle.attention(q, q[..., :3, :], q, True, 1.0)
+    with pytest.raises(RuntimeError):
+        oracle.attention(q, q, q, True, 1.0, rows=np.array([4]))
