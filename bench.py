@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the fused forward (attn_fwd_stream) over the metric's
+workload: causal, head dim 64, bf16 in / fp32 accumulate, B = 4 sequences x
+H = 12 heads x T = 8192 tokens, seeded N(0,1) inputs already resident in HBM
+("Flash attention in PyTorch, then in Triton" measures this shape on its
+RTX 4090, section "A kernel in Triton"). The FLOP count is the pages'
+convention, 2*B*H*T^2*D for causal attention (section "Attention by hand").
+
+Order of work, as the page "attention.cu" does it: the traffic arithmetic of
+both paths is printed first (stderr), then the output is checked against the
+double oracle on a seeded row sample (which is also the timed CPU baseline),
+and only then is anything timed. One JSON line goes to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention fwd TFLOP/s (causal, d=64, bf16, T=8192) and % of MFMA "
+          "peak")
+# MI355X published dense peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+BF16_TOL, F32_TOL_BASE = 2e-2, 1e-5
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "fused_bf16_causal_b4h12_t8192_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "online_softmax_amd", "csrc", f)
+                  for f in ("fused_fwd.hip", "fused_layout.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM-side bytes per launch from the committed PMC summary, if it was
+    taken on the kernel source as it is now; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            key, _, val = line.partition(":")
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def fmt_bytes(n):
+    return f"{n:>16,d} B  ({n / 2**20:10.2f} MiB)"
+
+
+def print_traffic(osa, w):
+    """Bytes before any time (the fused path, and the naive path's table
+    cost at this shape in fp32, which is the contrast)."""
+    dt = {"f32": osa.ATTN_F32, "bf16": osa.ATTN_BF16, "f16": osa.ATTN_F16}[w.dtype]
+    f = osa.attn_traffic_bytes(osa.ATTN_PATH_FUSED, w.B, w.H, w.T, w.D, dt,
+                               w.causal)
+    n = osa.attn_traffic_bytes(osa.ATTN_PATH_NAIVE, w.B, w.H, w.T, w.D,
+                               osa.ATTN_F32, w.causal)
+    log(f"traffic arithmetic, {w.name} (before any timing):")
+    log(f"  fused floor (Q,K,V,O once + lse) {fmt_bytes(f['floor'])}")
+    log(f"  fused ask (K,V per query tile)   {fmt_bytes(f['ask'])}")
+    log(f"  naive score-table passes (fp32)  {fmt_bytes(n['score_matrix'])}")
+    log(f"  naive table memory (fp32)        {fmt_bytes(n['table_bytes'])}")
+    log(f"  naive / fused floor traffic      {(n['score_matrix'] + n['floor']) / n['floor']:.1f}x")
+    return f, n
+
+
+def print_kernel_table(osa):
+    log(f"  {'kernel':28s} {'regs':>5s} {'LDS B':>7s} {'spill B':>8s} {'WG/CU':>6s}")
+    rows = {}
+    for i in range(osa.attn_kernel_count()):
+        a = osa.attn_kernel_attributes(i)
+        name = osa.attn_kernel_name(i)
+        rows[name] = a
+        log(f"  {name:28s} {a['num_regs']:5d} {a['lds_bytes']:7d} "
+            f"{a['private_bytes']:8d} {a['workgroups_per_cu']:6d}")
+    return rows
+
+
+def cpu_baseline(oracle, q, k, v, o, lse, w, nrows, seed):
+    """The double oracle, as it stands, on a seeded row sample of the same
+    workload: its rate (scaled to TFLOP/s by the rows' own visible keys) and
+    the GPU output's error on those rows."""
+    import numpy as np
+    from online_softmax_amd.inputs import sample_rows
+    rows = sample_rows(w.B, w.H, w.T, nrows, seed)
+    qn, kn, vn = (x.float().numpy() for x in (q, k, v))
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    ro, rl = oracle.attention(qn, kn, vn, w.causal, w.scale, rows=rows,
+                              threads=threads)
+    dt = time.perf_counter() - t0
+    t = rows % w.T
+    visible = (t + 1) if w.causal else np.full_like(t, w.T)
+    flops = float((4 * w.D * visible).sum())
+    got_o = o.reshape(-1, w.D).float().cpu().numpy()[rows]
+    got_l = lse.reshape(-1).cpu().numpy()[rows]
+    err_o = float(np.abs(got_o.astype(np.float64) - ro).max())
+    err_l = float(np.abs(got_l.astype(np.float64) - rl).max())
+    finite = bool(np.isfinite(got_o).all() and np.isfinite(got_l).all())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} seeded rows (of {w.rows}) of {w.name}, all "
+                   f"{w.D} dims, {flops:.3e} flop in {dt:.2f} s on {threads} "
+                   f"threads of {cpu_model()}"),
+    }, {"rows": int(len(rows)), "max_abs_err_o": err_o,
+        "max_abs_err_lse": err_l, "finite": finite}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def time_fused(osa, torch, q, k, v, o, lse, w, steps, warmup):
+    """W warm-up steps, then K timed steps bracketed by synchronisation;
+    each launch is also bracketed by HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        osa.attn_fwd_stream(q, k, v, o, lse, w.causal, w.scale, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        osa.attn_fwd_stream(q, k, v, o, lse, w.causal, w.scale, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return wall * 1e3 / steps, ms
+
+
+def contrast(osa, torch, oracle, steps=10):
+    """Both paths on the fp32 single-head workloads of the page
+    "attention.cu" (bytes first, then a correctness gate, then time)."""
+    from online_softmax_amd.inputs import WORKLOADS, workload_qkv
+    import numpy as np
+    out = []
+    for name in ("single_head_n1024_f32", "single_head_n4096_f32"):
+        w = WORKLOADS[name]
+        f = osa.attn_traffic_bytes(osa.ATTN_PATH_FUSED, 1, 1, w.T, 64,
+                                   osa.ATTN_F32, False)
+        n = osa.attn_traffic_bytes(osa.ATTN_PATH_NAIVE, 1, 1, w.T, 64,
+                                   osa.ATTN_F32, False)
+        log(f"{name}: naive score-table traffic {n['score_matrix']:,d} B, "
+            f"fused floor {f['floor']:,d} B, fused ask {f['ask']:,d} B")
+        q, k, v = (x.cuda() for x in workload_qkv(w))
+        o_f, o_n = torch.empty_like(q), torch.empty_like(q)
+        lse = torch.empty((1, 1, w.T), device=q.device)
+        ws = torch.empty(osa.attn_naive_workspace_bytes(1, 1, w.T),
+                         dtype=torch.uint8, device=q.device)
+        osa.attn_fwd_stream(q, k, v, o_f, lse, False, w.scale)
+        osa.attn_naive_fwd(q, k, v, o_n, None, ws, False, w.scale)
+        torch.cuda.synchronize()
+        ro, _ = oracle.attention(q.cpu(), k.cpu(), v.cpu(), False, w.scale)
+        bound = max(F32_TOL_BASE, F32_TOL_BASE * math.sqrt(w.T / 256))
+        ef = float(np.abs(o_f.cpu().numpy() - ro).max())
+        en = float(np.abs(o_n.cpu().numpy() - ro).max())
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        ms_f = timed(lambda: osa.attn_fwd_stream(q, k, v, o_f, lse, False,
+                                                 w.scale))
+        ms_n = timed(lambda: osa.attn_naive_fwd(q, k, v, o_n, None, ws, False,
+                                                w.scale))
+        fl = osa.attn_flops(1, 1, w.T, 64, False)
+        row = {"workload": name, "fused_ms": ms_f, "naive_ms": ms_n,
+               "fused_tflops": fl / ms_f / 1e9, "naive_tflops": fl / ms_n / 1e9,
+               "naive_table_traffic_B": n["score_matrix"],
+               "fused_floor_B": f["floor"], "fused_ask_B": f["ask"],
+               "max_abs_err_fused": ef, "max_abs_err_naive": en,
+               "bound": bound, "pass": ef <= bound and en <= bound}
+        log(f"  fused {ms_f:.4f} ms (err {ef:.2e}), naive {ms_n:.4f} ms "
+            f"(err {en:.2e}), naive/fused time {ms_n / ms_f:.1f}x")
+        out.append(row)
+        del q, k, v, o_f, o_n, ws
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="a name from online_softmax_amd.inputs.WORKLOADS")
+    ap.add_argument("--cpu-rows", type=int, default=32768,
+                    help="oracle sample size for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-contrast", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB "
+                         "(reference kernel for PMC byte counters)")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}): the attention forward of one GPU's share "
+              "is the whole workload here; no multi-GPU figure is produced.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import online_softmax_amd as osa
+    from online_softmax_amd.inputs import METRIC_WORKLOAD, WORKLOADS, workload_qkv
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    osa.load()
+    w = WORKLOADS[a.workload or METRIC_WORKLOAD]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"GPU: {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs")
+    traffic_f, _ = print_traffic(osa, w)
+    kernels = print_kernel_table(osa)
+
+    q, k, v = workload_qkv(w)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+
+    cpu, parity = None, None
+    if not a.no_cpu_baseline:
+        import oracle
+        log(f"oracle on {a.cpu_rows} sampled rows (correctness gate and CPU "
+            "baseline) ...")
+        cpu, parity = cpu_baseline(oracle, q, k, v, o, lse, w, a.cpu_rows, 9001)
+        bound = BF16_TOL if w.dtype != "f32" else max(
+            F32_TOL_BASE, F32_TOL_BASE * math.sqrt(w.T / 256))
+        parity["bound"] = bound
+        parity["pass"] = (parity["finite"] and parity["max_abs_err_o"] <= bound
+                          and parity["max_abs_err_lse"] <= bound)
+        log(f"  parity on sample: {parity}")
+        log(f"  oracle: {cpu['value'] * 1e3:.2f} GFLOP/s ({cpu['sample']})")
+        if not parity["pass"]:
+            log("correctness gate FAILED: not timing a wrong kernel")
+            sys.exit(3)
+
+    ms_step, launch_ms = time_fused(osa, torch, qd, kd, vd, o, lse, w,
+                                    a.steps, a.warmup)
+    flops = osa.attn_flops(w.B, w.H, w.T, w.D, w.causal)
+    value = flops / (ms_step * 1e-3) / 1e12
+    avg_launch = statistics.fmean(launch_ms)
+    achieved = flops / (avg_launch * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"fused: {ms_step:.4f} ms/step wall, launch median "
+        f"{statistics.median(launch_ms):.4f} ms (min {min(launch_ms):.4f}, mean "
+        f"{avg_launch:.4f}), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% "
+        f"of {peak} TFLOP/s")
+
+    if a.copy_mib > 0:  # reference kernel of known size for byte counters
+        src = torch.empty(a.copy_mib * 2**20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {a.copy_mib} MiB x 3 (PMC reference)")
+
+    extra = None
+    if not a.no_contrast:
+        import oracle
+        extra = contrast(osa, torch, oracle)
+
+    kname = osa.attn_kernel_name({"bf16": 0, "f16": 2, "f32": 4}[w.dtype] +
+                                 (0 if w.causal else 1))
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded torch.randn N(0,1) fp32, rounded (RNE) to "
+                f"{w.dtype}",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(),
+                     "kernel": kname,
+                     "launch_ms": {"mean": avg_launch,
+                                   "median": statistics.median(launch_ms),
+                                   "min": min(launch_ms)},
+                     "algorithmic_flop_per_launch": flops,
+                     "traffic_arith_B": traffic_f},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "kernels": kernels,
+        "contrast_fp32_single_head": extra,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

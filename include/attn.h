@@ -1,0 +1,182 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn.so).
+ *
+ * The operation is exact scaled-dot-product attention for head dimension 64,
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,h,j,:] ) v[b,h,j,:]
+ *
+ * over the keys j visible to query i (all j < T, or j <= i when causal), plus
+ * the per-row log-sum-exp  lse[b,h,i] = log sum_j exp(scale * q_i . k_j)  in
+ * natural-log units. Definitions: "Flash attention in PyTorch, then in
+ * Triton", section "Attention's table of scores" (scores, causal mask,
+ * softmax, weighted values) and section "Backwards, and training with it"
+ * (the per-row log-sum-exp the forward pass keeps). The fused path computes it
+ * the way that page's section "Flash attention" describes (the online
+ * softmax: key tiles with a running maximum, denominator and output, rescaled
+ * when a larger maximum arrives), so the T x T score table never exists. The
+ * naive path is the materialising contrast of the page "attention.cu" (a
+ * tiled Q K^T into a T x T buffer, a max pass and an exp-and-sum pass into a
+ * second buffer, then a tiled P V divided by the row sums).
+ *
+ * Conventions shared by every entry point:
+ *  - Layout: q, k, v, o are contiguous row-major [B, H, T, D] arrays of the
+ *    element type `dtype` (element (b,h,t,e) at ((b*H + h)*T + t)*D + e);
+ *    lse is a contiguous float32 [B, H, T] array.
+ *  - Memory: q, k, v, o, lse, workspace are DEVICE pointers on the current
+ *    HIP device. The caller owns every buffer; the library allocates nothing
+ *    and keeps no pointer after the call returns.
+ *  - Alignment: q, k, v, o and workspace must be 16-byte aligned (the kernels
+ *    use 128-bit accesses); lse must be 4-byte aligned.
+ *  - Streams: `stream` is a hipStream_t (NULL means the null stream). Calls
+ *    return once the work is enqueued; the results are ready after the
+ *    stream is synchronised. A fault inside a kernel surfaces at that
+ *    synchronisation, not as a return code.
+ *  - Errors: every entry point returns an attn_status. Arguments are checked
+ *    before any HIP call, so an invalid call has no side effect and touches
+ *    no device. The library never prints and never exits.
+ *  - Threads: calls are re-entrant; attn_last_hip_error() is per thread.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. lse is always float32. */
+typedef enum {
+    ATTN_F32 = 0,  /* float32; products on the fp32 matrix cores          */
+    ATTN_BF16 = 1, /* bfloat16 in, float32 accumulate, bfloat16 out       */
+    ATTN_F16 = 2   /* float16 in, float32 accumulate, float16 out         */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = -1,     /* a null or misaligned pointer, a size < 1,
+                                  an unknown dtype, a non-finite scale, a
+                                  workspace too small, a null output struct */
+    ATTN_ERR_UNSUPPORTED = -2, /* a well-formed request this library does not
+                                  implement: D != 64, a non-fp32 naive call,
+                                  or a grid larger than one launch holds     */
+    ATTN_ERR_HIP = -3          /* the HIP runtime refused a launch or query;
+                                  the code is kept for attn_last_hip_error() */
+} attn_status;
+
+typedef enum { ATTN_PATH_FUSED = 0, ATTN_PATH_NAIVE = 1 } attn_path;
+
+/*
+ * attn_fwd_stream - fused attention forward (online softmax, no T x T table).
+ *
+ * q, k, v : device, [B, H, T, D] of `dtype`, read only.
+ * o       : device, [B, H, T, D] of `dtype`, written (every element).
+ * lse     : device, float32 [B, H, T], written; may be NULL to skip it.
+ * B, H, T : batch, heads, tokens; each >= 1. Queries and keys share T.
+ * D       : head dimension; must be 64.
+ * causal  : nonzero => key j is visible to query i iff j <= i (top-left
+ *           aligned); zero => every key is visible.
+ * scale   : multiplies q . k before the softmax (usually 1/sqrt(D)); any
+ *           finite value, including 0 and negative values.
+ * dtype   : an attn_dtype.
+ * stream  : hipStream_t or NULL.
+ *
+ * Returns ATTN_OK once enqueued, or an error status with nothing enqueued.
+ * Extra device memory: none (the caller's lse is the only O(T) side output).
+ */
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int T, int D, int causal,
+                    float scale, int dtype, void* stream);
+
+/* attn_fwd - attn_fwd_stream on the null stream. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int T, int D, int causal, float scale, int dtype);
+
+/*
+ * attn_naive_fwd - the materialising contrast path, float32 only.
+ *
+ * Same meaning for q, k, v, o, lse, B, H, T, D, causal, scale and stream as
+ * attn_fwd_stream (lse may be NULL). workspace is a caller-owned device
+ * buffer of at least attn_naive_workspace_bytes(B, H, T) bytes; it receives
+ * the score table S [B,H,T,T], the exponential table P [B,H,T,T] and the row
+ * sums [B,H,T], all float32, and its contents are undefined afterwards.
+ * Returns ATTN_ERR_UNSUPPORTED for dtype != ATTN_F32 (the dtype argument is
+ * part of the signature so the two paths take the same arguments).
+ */
+int attn_naive_fwd(const float* q, const float* k, const float* v, float* o,
+                   float* lse, void* workspace, size_t workspace_bytes, int B,
+                   int H, int T, int D, int causal, float scale, int dtype,
+                   void* stream);
+
+/* Workspace bytes attn_naive_fwd needs: (2*B*H*T*T + B*H*T) * 4 rounded up
+ * to 256 bytes; 0 for sizes < 1 or when the count overflows 64 bits. */
+size_t attn_naive_workspace_bytes(int B, int H, int T);
+
+/*
+ * Memory traffic of one call, as arithmetic (no device is touched). The
+ * page "attention.cu" prints these counts before any time is measured.
+ *
+ *   floor        : Q, K, V read once and O written once, plus the lse row
+ *                  values (4 bytes per row) - the least any exact path moves.
+ *   ask          : bytes the path's kernels request from global memory as
+ *                  launched (fused: Q once, O and lse once, and K and V once
+ *                  per query tile that reads them; naive: see below). Whether
+ *                  a request reaches DRAM or hits a cache is not modelled.
+ *   score_matrix : naive only - bytes spent on the T x T tables: S written,
+ *                  S read twice, P written, P read once (5 passes of
+ *                  4*T*T bytes per head); 0 for the fused path.
+ *   table_bytes  : naive only - bytes of device memory the tables occupy
+ *                  (the workspace); 0 for the fused path.
+ */
+typedef struct {
+    uint64_t floor;
+    uint64_t ask;
+    uint64_t score_matrix;
+    uint64_t table_bytes;
+} attn_traffic;
+
+int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
+                       int causal, attn_traffic* out);
+
+/* Arithmetic convention for throughput: each of the two products costs
+ * 2*T*T*D flops per head (a multiply and an add), with half the table
+ * masked away when causal: 4*B*H*T*T*D non-causal, 2*B*H*T*T*D causal
+ * ("Flash attention in PyTorch, then in Triton", section "Attention by
+ * hand"). Returned as a double; 0 for sizes < 1. */
+double attn_flops(int B, int H, int T, int D, int causal);
+
+/* Static text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* The hipError_t of the calling thread's last ATTN_ERR_HIP (0 if none). */
+int attn_last_hip_error(void);
+
+/*
+ * Per-kernel resource figures from the HIP runtime (registers, LDS, resident
+ * workgroups per compute unit), the same table "attention.cu" prints from
+ * its runtime API. kernel ranges over [0, attn_kernel_count()). Needs a GPU;
+ * returns ATTN_ERR_HIP without one.
+ */
+typedef struct {
+    int num_regs;              /* vector registers per lane               */
+    int lds_bytes;             /* static LDS per workgroup                */
+    int private_bytes;         /* per-lane scratch (spills); 0 is healthy */
+    int threads_per_workgroup; /* launch width used by the library        */
+    int workgroups_per_cu;     /* occupancy API, at that width            */
+} attn_kernel_attr;
+
+int attn_kernel_count(void);
+const char* attn_kernel_name(int kernel);
+int attn_kernel_attributes(int kernel, attn_kernel_attr* out);
+
+/* Tile geometry of the fused path, for traffic arithmetic and tests:
+ * queries per workgroup and keys per LDS tile for `dtype`. */
+int attn_fused_tile(int dtype, int* block_m, int* block_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,222 @@
+"""ctypes binding of libattn.so (include/attn.h), argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes
+torch tensors where the C function takes device pointers; it derives the
+sizes and the dtype code from the tensors, passes the current HIP stream
+unless one is given, and raises AttnError for a non-OK status. No step of
+the computation happens here, and there is no fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libattn.so")
+
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
+ATTN_PATH_FUSED, ATTN_PATH_NAIVE = 0, 1
+
+# every symbol include/attn.h declares
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
+           "attn_naive_workspace_bytes", "attn_traffic_bytes", "attn_flops",
+           "attn_status_string", "attn_last_hip_error", "attn_kernel_count",
+           "attn_kernel_name", "attn_kernel_attributes", "attn_fused_tile")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = _lib().attn_status_string(status).decode()
+        hip = _lib().attn_last_hip_error() if status == ATTN_ERR_HIP else 0
+        super().__init__(f"{where}: {text} ({status})" +
+                         (f", hipError {hip}" if hip else ""))
+
+
+class attn_traffic(ctypes.Structure):
+    _fields_ = [("floor", ctypes.c_uint64), ("ask", ctypes.c_uint64),
+                ("score_matrix", ctypes.c_uint64),
+                ("table_bytes", ctypes.c_uint64)]
+
+
+class attn_kernel_attr(ctypes.Structure):
+    _fields_ = [("num_regs", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("private_bytes", ctypes.c_int),
+                ("threads_per_workgroup", ctypes.c_int),
+                ("workgroups_per_cu", ctypes.c_int)]
+
+
+_lock = threading.Lock()
+_handle = None
+
+
+def load(path: str = LIBRARY):
+    """Load the in-tree libattn.so; raises if it has not been built."""
+    global _handle
+    with _lock:
+        if _handle is not None and path == LIBRARY:
+            return _handle
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with "
+                "`python -m online_softmax_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(path)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_fwd_stream.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+        lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I]
+        lib.attn_naive_fwd.argtypes = [P, P, P, P, P, P, S, I, I, I, I, I, F,
+                                       I, P]
+        lib.attn_naive_workspace_bytes.argtypes = [I, I, I]
+        lib.attn_naive_workspace_bytes.restype = S
+        lib.attn_traffic_bytes.argtypes = [I, I, I, I, I, I, I,
+                                           ctypes.POINTER(attn_traffic)]
+        lib.attn_flops.argtypes = [I, I, I, I, I]
+        lib.attn_flops.restype = ctypes.c_double
+        lib.attn_status_string.argtypes = [I]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_last_hip_error.argtypes = []
+        lib.attn_kernel_count.argtypes = []
+        lib.attn_kernel_name.argtypes = [I]
+        lib.attn_kernel_name.restype = ctypes.c_char_p
+        lib.attn_kernel_attributes.argtypes = [I, ctypes.POINTER(attn_kernel_attr)]
+        lib.attn_fused_tile.argtypes = [I, ctypes.POINTER(I), ctypes.POINTER(I)]
+        for name in EXPORTS:  # fail here, not at first use, if one is absent
+            getattr(lib, name)
+        if path == LIBRARY:
+            _handle = lib
+        return lib
+
+
+def _lib():
+    return load()
+
+
+def _check(status: int, where: str):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16,
+             torch.float16: ATTN_F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream)) if stream else None
+
+
+def _dims(q):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, D]")
+    return tuple(int(x) for x in q.shape)
+
+
+def attn_fwd_stream(q, k, v, o, lse, causal: bool, scale: float, stream=None):
+    """Fused forward into caller-owned o ([B,H,T,D], q's dtype) and lse
+    ([B,H,T] float32 or None) on `stream` (default: the current stream)."""
+    B, H, T, D = _dims(q)
+    st = _lib().attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                B, H, T, D, int(bool(causal)), float(scale),
+                                dtype_code(q), _stream(stream, q.device))
+    _check(st, "attn_fwd_stream")
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float):
+    """Fused forward on the null stream."""
+    B, H, T, D = _dims(q)
+    st = _lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                         T, D, int(bool(causal)), float(scale), dtype_code(q))
+    _check(st, "attn_fwd")
+
+
+def attn_naive_workspace_bytes(B: int, H: int, T: int) -> int:
+    return int(_lib().attn_naive_workspace_bytes(B, H, T))
+
+
+def attn_naive_fwd(q, k, v, o, lse, workspace, causal: bool, scale: float,
+                   stream=None):
+    """Materialising fp32 path; workspace is a caller-owned device tensor of
+    at least attn_naive_workspace_bytes(B, H, T) bytes."""
+    B, H, T, D = _dims(q)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib().attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               _ptr(workspace), nbytes, B, H, T, D,
+                               int(bool(causal)), float(scale), dtype_code(q),
+                               _stream(stream, q.device))
+    _check(st, "attn_naive_fwd")
+
+
+def attn_traffic_bytes(path: int, B: int, H: int, T: int, D: int, dtype: int,
+                       causal: bool) -> dict:
+    out = attn_traffic()
+    st = _lib().attn_traffic_bytes(path, B, H, T, D, dtype, int(bool(causal)),
+                                   ctypes.byref(out))
+    _check(st, "attn_traffic_bytes")
+    return {f: int(getattr(out, f)) for f, _ in attn_traffic._fields_}
+
+
+def attn_flops(B: int, H: int, T: int, D: int, causal: bool) -> float:
+    return float(_lib().attn_flops(B, H, T, D, int(bool(causal))))
+
+
+def attn_fused_tile(dtype: int):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(_lib().attn_fused_tile(dtype, ctypes.byref(bm), ctypes.byref(bn)),
+           "attn_fused_tile")
+    return bm.value, bn.value
+
+
+def attn_status_string(status: int) -> str:
+    return _lib().attn_status_string(status).decode()
+
+
+def attn_last_hip_error() -> int:
+    return int(_lib().attn_last_hip_error())
+
+
+def attn_kernel_count() -> int:
+    return int(_lib().attn_kernel_count())
+
+
+def attn_kernel_name(kernel: int) -> str:
+    r = _lib().attn_kernel_name(kernel)
+    return None if r is None else r.decode()
+
+
+def attn_kernel_attributes(kernel: int) -> dict:
+    out = attn_kernel_attr()
+    _check(_lib().attn_kernel_attributes(kernel, ctypes.byref(out)),
+           "attn_kernel_attributes")
+    return {f: int(getattr(out, f)) for f, _ in attn_kernel_attr._fields_}
+
+
+def attention(q, k, v, causal: bool = True, scale: float | None = None,
+              with_lse: bool = True, stream=None):
+    """Allocate o (and lse) with torch on q's device and run the fused path.
+    Returns (o, lse)."""
+    import torch
+    B, H, T, D = _dims(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) \
+        if with_lse else None
+    attn_fwd_stream(q, k, v, o, lse, causal, scale, stream)
+    return o, lse

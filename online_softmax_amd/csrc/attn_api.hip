@@ -1,0 +1,235 @@
+// The C ABI (include/attn.h): argument validation, dispatch to the kernels,
+// traffic arithmetic and runtime queries. Every check runs before the first
+// HIP call, so invalid calls are side-effect free and testable without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn.h"
+#include "fused_layout.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) {
+    return dtype == ATTN_F32 || dtype == ATTN_BF16 || dtype == ATTN_F16;
+}
+
+// 64-bit product with overflow detection (all operands >= 0).
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    if (a != 0 && b > UINT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Shape checks shared by both paths. Returns ATTN_OK or an error status.
+int check_shape(int B, int H, int T, int D) {
+    if (B < 1 || H < 1 || T < 1 || D < 1) return ATTN_ERR_INVALID;
+    if (D != attn::kHeadDim) return ATTN_ERR_UNSUPPORTED;
+    uint64_t bh, elems;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || bh > (uint64_t)INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
+    if (!mul_ok(bh * (uint64_t)T, (uint64_t)D, &elems)) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Largest 1-D grid one fused launch takes: workgroups * 256 threads must
+// stay below 2^32.
+constexpr uint64_t kMaxFusedWorkgroups = (1ull << 24) - 1;
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int T, int D, int causal,
+                    float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return ATTN_ERR_INVALID;
+    if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
+    const uint64_t nq = ((uint64_t)T + attn::kBlockM - 1) / attn::kBlockM;
+    if (nq * (uint64_t)B * (uint64_t)H > kMaxFusedWorkgroups)
+        return ATTN_ERR_UNSUPPORTED;
+    // exp2 multiplier: |scale| * log2(e); a negative scale negates Q instead
+    const double c = fabs((double)scale) * 1.4426950408889634073599;
+    if (!isfinite((float)c)) return ATTN_ERR_INVALID;
+    const hipError_t e = attn::launch_fused(
+        q, k, v, o, lse, B * H, T, causal ? 1 : 0, (float)c, scale < 0.0f,
+        dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int T, int D, int causal, float scale, int dtype) {
+    return attn_fwd_stream(q, k, v, o, lse, B, H, T, D, causal, scale, dtype,
+                           nullptr);
+}
+
+size_t attn_naive_workspace_bytes(int B, int H, int T) {
+    if (B < 1 || H < 1 || T < 1) return 0;
+    uint64_t bh, tt, table, two, rows, total;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh)) return 0;
+    if (!mul_ok((uint64_t)T, (uint64_t)T, &tt)) return 0;
+    if (!mul_ok(bh, tt, &table)) return 0;
+    if (!mul_ok(table, 2, &two)) return 0;
+    rows = bh * (uint64_t)T;
+    if (two + rows < two) return 0;
+    if (!mul_ok(two + rows, 4, &total)) return 0;
+    if (total > UINT64_MAX - 255) return 0;
+    return (size_t)((total + 255) & ~(uint64_t)255);
+}
+
+int attn_naive_fwd(const float* q, const float* k, const float* v, float* o,
+                   float* lse, void* workspace, size_t workspace_bytes, int B,
+                   int H, int T, int D, int causal, float scale, int dtype,
+                   void* stream) {
+    if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(workspace))
+        return ATTN_ERR_INVALID;
+    if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
+    const size_t need = attn_naive_workspace_bytes(B, H, T);
+    if (need == 0) return ATTN_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return ATTN_ERR_INVALID;
+    // grid limits of the three kernels: y and z dimensions stay <= 65535
+    const uint64_t tiles = ((uint64_t)T + 63) / 64;
+    if ((uint64_t)B * H > 65535 || tiles > 65535) return ATTN_ERR_UNSUPPORTED;
+    const uint64_t table = (uint64_t)B * H * T * T;
+    float* s = (float*)workspace;
+    float* p = s + table;
+    float* rowsum = p + table;
+    const hipError_t e =
+        attn::launch_naive(q, k, v, o, lse, s, p, rowsum, B * H, T,
+                           causal ? 1 : 0, scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
+int attn_fused_tile(int dtype, int* block_m, int* block_n) {
+    if (!valid_dtype(dtype) || !block_m || !block_n) return ATTN_ERR_INVALID;
+    *block_m = attn::kBlockM;
+    *block_n = dtype == ATTN_F32 ? attn::kBlockN32 : attn::kBlockN16;
+    return ATTN_OK;
+}
+
+int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
+                       int causal, attn_traffic* out) {
+    if (!out) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (path != ATTN_PATH_FUSED && path != ATTN_PATH_NAIVE)
+        return ATTN_ERR_INVALID;
+    if (path == ATTN_PATH_NAIVE && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t elt = (uint64_t)elem_bytes(dtype);
+    const uint64_t row_bytes = (uint64_t)D * elt;   // one row of q/k/v/o
+    const uint64_t tensor = bh * (uint64_t)T * row_bytes;
+    const uint64_t lse_bytes = bh * (uint64_t)T * 4;
+    attn_traffic r;
+    memset(&r, 0, sizeof(r));
+    r.floor = 4 * tensor + lse_bytes;
+    if (path == ATTN_PATH_FUSED) {
+        // K and V rows each query tile loads (rows >= T are never fetched)
+        int bm, bn;
+        attn_fused_tile(dtype, &bm, &bn);
+        const int nq = (T + bm - 1) / bm;
+        uint64_t kv_rows = 0;
+        for (int qt = 0; qt < nq; ++qt) {
+            const int tiles = attn::key_tiles(qt, T, bn, causal != 0);
+            const uint64_t rows = (uint64_t)tiles * bn;
+            kv_rows += rows < (uint64_t)T ? rows : (uint64_t)T;
+        }
+        r.ask = 2 * tensor + lse_bytes + 2 * bh * kv_rows * row_bytes;
+    } else {
+        const uint64_t tt = (uint64_t)T * T;
+        r.score_matrix = 5 * 4 * bh * tt;
+        r.table_bytes = attn_naive_workspace_bytes(B, H, T);
+        // scores: each 64 x 64 tile reads a 64-row block of Q and of K;
+        // weighted V: each 64-row block reads all of V; row sums written and
+        // read once; O and lse written once.
+        const uint64_t tiles = ((uint64_t)T + 63) / 64;
+        r.ask = r.score_matrix + 2 * tensor * tiles + tensor * tiles +
+                2 * lse_bytes + tensor + lse_bytes;
+    }
+    *out = r;
+    return ATTN_OK;
+}
+
+double attn_flops(int B, int H, int T, int D, int causal) {
+    if (B < 1 || H < 1 || T < 1 || D < 1) return 0.0;
+    const double full = 4.0 * B * H * (double)T * (double)T * D;
+    return causal ? full / 2.0 : full;
+}
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported request";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_kernel_count(void) { return attn::kFusedKernels + attn::kNaiveKernels; }
+
+const char* attn_kernel_name(int kernel) {
+    static const char* const names[] = {
+        "fused_fwd16<bf16, causal>", "fused_fwd16<bf16, full>",
+        "fused_fwd16<f16, causal>",  "fused_fwd16<f16, full>",
+        "fused_fwd32<causal>",       "fused_fwd32<full>",
+        "naive_scores",              "naive_softmax",
+        "naive_weighted_v"};
+    if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
+    return names[kernel];
+}
+
+int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
+    if (!out || kernel < 0 || kernel >= attn_kernel_count())
+        return ATTN_ERR_INVALID;
+    const void* fn = kernel < attn::kFusedKernels
+                         ? attn::fused_kernel_ptr(kernel)
+                         : attn::naive_kernel_ptr(kernel - attn::kFusedKernels);
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
+    if (e != hipSuccess) return hip_fail(e);
+    const int threads = 256;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    out->num_regs = fa.numRegs;
+    out->lds_bytes = (int)fa.sharedSizeBytes;
+    out->private_bytes = (int)fa.localSizeBytes;
+    out->threads_per_workgroup = threads;
+    out->workgroups_per_cu = per_cu;
+    return ATTN_OK;
+}
+
+}  // extern "C"

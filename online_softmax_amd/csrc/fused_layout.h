@@ -1,0 +1,165 @@
+// Tile geometry and every index computation of the fused attention kernels.
+//
+// All address arithmetic of the fused kernels goes through the functions in
+// this header, which compile for the host as well as the device, so a CPU
+// test can enumerate every thread, tile and fragment of a launch and check
+// that each global and LDS access stays inside its buffer before a kernel is
+// ever run.
+//
+// Work split (the query-block split of FlashAttention-2 that "Flash
+// attention in PyTorch, then in Triton" uses, section "A kernel in Triton"):
+// one workgroup of 4 wave64s owns kBlockM = 128 consecutive query rows of
+// one (batch, head) slice; each wave owns 32 of them and walks the key tiles
+// in ascending order.
+//
+// MFMA orientation. The score tile is computed transposed, S^T = K * Q^T, on
+// 32x32 MFMAs: the A operand is a K fragment (row = key), the B operand a Q
+// fragment (column = query). An MFMA accumulator register r of lane l holds
+// row 8*(r/4) + 4*(l/32) + (r%4), column l%32, so every lane owns ONE query
+// (l % 32) and 16 of the 32 keys of a 32x32 tile; the other 16 keys of that
+// query sit in lane l ^ 32. Row max and row sum are in-lane reductions plus
+// one exchange between the two 32-lane halves. The output is accumulated
+// transposed the same way, O^T = V^T * P^T, so the per-query rescale factor
+// is a per-lane scalar.
+//
+// K-index freedom. An MFMA pairs slot s of lane-half h of its A operand with
+// slot s of lane-half h of its B operand for the same reduction index, so any
+// assignment of reduction indices to (half, slot) works as long as A and B
+// use the same one. The P fragment inherits its key order from the
+// accumulator layout; the transposed V tile in LDS stores its keys in the
+// matching order (vt_pos16) so a lane's 8 keys are 16 contiguous bytes.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define ATTN_HD __host__ __device__ inline
+#else
+#define ATTN_HD inline
+#endif
+
+namespace attn {
+
+constexpr int kHeadDim = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
+
+// ---- 16-bit (bf16 / f16) path -------------------------------------------
+constexpr int kBlockN16 = 64;     // keys per LDS tile
+constexpr int kLdsStride16 = 72;  // elements per LDS row: 64 + 8 pad (16 B)
+constexpr int kKTile16 = kBlockN16 * kLdsStride16;    // K tile, elements
+constexpr int kVTile16 = kHeadDim * kLdsStride16;     // V^T tile, elements
+
+// ---- fp32 path -----------------------------------------------------------
+constexpr int kBlockN32 = 32;
+constexpr int kKStride32 = 68;    // floats per K row: 64 + 4 pad
+constexpr int kVStride32 = 36;    // floats per V^T row: 32 + 4 pad
+constexpr int kKTile32 = kBlockN32 * kKStride32;
+constexpr int kVTile32 = kHeadDim * kVStride32;
+
+static_assert(kLdsStride16 % 8 == 0, "16-bit LDS rows must stay 16-byte aligned");
+static_assert(kKStride32 % 4 == 0 && kVStride32 % 4 == 0,
+              "fp32 LDS rows must stay 16-byte aligned");
+static_assert(2 * 2 * (kKTile16 + kVTile16) <= 64 * 1024,
+              "16-bit double-buffered K and V^T tiles must fit 64 KiB");
+static_assert(2 * 4 * (kKTile32 + kVTile32) <= 64 * 1024,
+              "fp32 double-buffered K and V^T tiles must fit 64 KiB");
+
+// Row (key or head-dim index) held by accumulator register r of a lane in
+// lane-half h of a 32x32 MFMA output tile.
+ATTN_HD int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Column of key `key` (0..63 within a tile) in the transposed V tile of the
+// 16-bit path: bits 2 and 3 of the key index are swapped, which puts the 8
+// keys a lane-half feeds one PV MFMA next to each other.
+ATTN_HD int vt_pos16(int key) {
+    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// Workgroup -> (slice bh, query tile qt). Workgroups are dealt round-robin
+// to the 8 XCDs, so when the count divides by 8 the consecutive logical tiles
+// are regrouped to land on one XCD: each XCD walks whole (batch, head)
+// slices, and the slice's K and V stay in that XCD's L2. Causal launches
+// take the heaviest (last) query tile of a slice first.
+ATTN_HD void tile_of(int block, int total, int nq, bool causal, int* bh,
+                     int* qt) {
+    int L = block;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        L = (block & 7) * per + (block >> 3);
+    }
+    *bh = L / nq;
+    const int t = L - *bh * nq;
+    *qt = causal ? nq - 1 - t : t;
+}
+
+// Number of key tiles of `bn` keys query tile qt reads: every tile that
+// holds a key visible to one of its valid rows (rows < T).
+ATTN_HD int key_tiles(int qt, int T, int bn, bool causal) {
+    const int all = (T + bn - 1) / bn;
+    if (!causal) return all;
+    int last = qt * kBlockM + kBlockM - 1;
+    if (last > T - 1) last = T - 1;
+    const int n = last / bn + 1;
+    return n < all ? n : all;
+}
+
+// ---- 16-bit staging: global -> registers -> LDS ---------------------------
+// K tile: 64 keys x 64 dims = 512 chunks of 16 B; thread t moves chunks
+// t and t + 256 (i = 0, 1): key row and first dim of chunk i.
+ATTN_HD void k_stage16(int t, int i, int* row, int* col) {
+    const int c = t + kThreads * i;
+    *row = c >> 3;
+    *col = (c & 7) * 8;
+}
+ATTN_HD int k_lds16(int row, int col) { return row * kLdsStride16 + col; }
+
+// V tile: thread t loads keys key0, key0 + 1 at dims dim0 .. dim0 + 7 and
+// writes them transposed (one 32-bit pair per dim). Lanes of a wave differ
+// in the key pair first so the 32-bit LDS writes fall on distinct banks.
+ATTN_HD void v_stage16(int t, int* key0, int* dim0) {
+    *key0 = 2 * (t & 31);
+    *dim0 = 8 * (t >> 5);
+}
+ATTN_HD int v_lds16(int dim, int key) {
+    return dim * kLdsStride16 + vt_pos16(key);
+}
+
+// Q fragment of lane-half h for reduction step ks: dims 16*ks + 8*h .. +7.
+ATTN_HD int q_col16(int h, int ks) { return 16 * ks + 8 * h; }
+// K fragment (A operand of S^T tile nt, step ks) read by lane (ql, h).
+ATTN_HD int kfrag16(int ql, int h, int nt, int ks) {
+    return (32 * nt + ql) * kLdsStride16 + 16 * ks + 8 * h;
+}
+// V^T fragment (A operand of O^T tile mt, step ks) read by lane (ql, h).
+ATTN_HD int vfrag16(int ql, int h, int mt, int ks) {
+    return (32 * mt + ql) * kLdsStride16 + 16 * ks + 8 * h;
+}
+
+// ---- fp32 staging ----------------------------------------------------------
+// K tile: 32 keys x 64 dims = 512 chunks of 16 B; chunks t and t + 256.
+ATTN_HD void k_stage32(int t, int i, int* row, int* col) {
+    const int c = t + kThreads * i;
+    *row = c >> 4;
+    *col = (c & 15) * 4;
+}
+ATTN_HD int k_lds32(int row, int col) { return row * kKStride32 + col; }
+// V tile: keys key0, key0 + 1 at dims dim0 .. dim0 + 3, written transposed
+// as one 64-bit pair per dim.
+ATTN_HD void v_stage32(int t, int* key0, int* dim0) {
+    *key0 = 2 * (t & 15);
+    *dim0 = 4 * (t >> 4);
+}
+ATTN_HD int v_lds32(int dim, int key) { return dim * kVStride32 + key; }
+// Q fragment of lane-half h, group g: dims 8*g + 4*h .. +3 (one MFMA step
+// per dim, two steps' worth of dims per lane pair).
+ATTN_HD int q_col32(int h, int g) { return 8 * g + 4 * h; }
+ATTN_HD int kfrag32(int ql, int h, int g) {
+    return ql * kKStride32 + 8 * g + 4 * h;
+}
+ATTN_HD int vfrag32(int ql, int h, int mt, int g) {
+    return (32 * mt + ql) * kVStride32 + 8 * g + 4 * h;
+}
+
+}  // namespace attn

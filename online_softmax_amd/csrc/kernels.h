@@ -1,0 +1,33 @@
+// Internal launchers shared by the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// element type codes (match attn_dtype in include/attn.h)
+#define ATTN_DT_F32 0
+#define ATTN_DT_BF16 1
+#define ATTN_DT_F16 2
+
+namespace attn {
+
+// Fused online-softmax forward over BH = B*H slices of T rows each.
+// c = |scale| * log2(e); negate_q flips the sign of Q (for scale < 0).
+hipError_t launch_fused(const void* q, const void* k, const void* v, void* o,
+                        float* lse, int BH, int T, int causal, float c,
+                        bool negate_q, int dt, hipStream_t stream);
+
+// Materialising fp32 path. s, p: [BH, T, T]; rowsum: [BH, T].
+hipError_t launch_naive(const float* q, const float* k, const float* v,
+                        float* o, float* lse, float* s, float* p,
+                        float* rowsum, int BH, int T, int causal, float scale,
+                        hipStream_t stream);
+
+// Kernel table for attribute queries.
+constexpr int kFusedKernels = 6;
+constexpr int kNaiveKernels = 3;
+const void* fused_kernel_ptr(int index);
+const void* naive_kernel_ptr(int index);
+
+}  // namespace attn

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP kernels (called through the C ABI) against the double
+oracle, element by element, on the same seeded inputs.
+
+Tolerances (max |delta| over every checked element of O and of lse):
+  fp32      : max(1e-5, 1e-5 * sqrt(T / 256))
+  bf16, f16 : 2e-2, against the oracle run on the same rounded inputs
+Any non-finite output fails. Shapes follow the five workloads of the pages
+(one fp32 head at 256 / 1024 / 4096 tokens from "attention.cu"; two
+sequences of three heads at 1 / 100 / 256 / 1000 tokens and the ragged 16-bit
+lengths 1 / 77 / 128 / 300 / 1024 from "Flash attention in PyTorch, then in
+Triton"; the GPT-2-small-shaped 4 x 12 x 8192 bf16 causal case; and the long
+16-head cases), plus closed-form and stress inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_amd.inputs import (WORKLOADS, late_spike_qkv, make_qkv,
+                                       sample_rows, workload_qkv)
+from conftest import flush_print
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D = 64
+
+
+def tol(dtype: str, T: int) -> float:
+    return max(1e-5, 1e-5 * math.sqrt(T / 256.0)) if dtype == "f32" else 2e-2
+
+
+def fused(lib, q, k, v, causal, scale, with_lse=True):
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o, lse = lib.attention(qd, kd, vd, causal, scale, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return o.float().cpu(), (lse.cpu() if lse is not None else None)
+
+
+def naive(lib, q, k, v, causal, scale):
+    B, H, T, _ = q.shape
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    ws = torch.empty(lib.attn_naive_workspace_bytes(B, H, T), dtype=torch.uint8,
+                     device=DEV)
+    lib.attn_naive_fwd(qd, kd, vd, o, lse, ws, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def assert_close(name, got, want, bound):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = np.abs(got - want)
+    worst = int(np.argmax(err)) if err.size else 0
+    mx = float(err.max()) if err.size else 0.0
+    flush_print(f"    {name}: max|d| = {mx:.3e} (bound {bound:.1e})")
+    assert mx <= bound, (f"{name}: max|d| {mx:.3e} > {bound:.1e} at flat "
+                         f"index {worst}: got {got.flat[worst]!r} want "
+                         f"{want.flat[worst]!r}")
+
+
+def check_full(lib, q, k, v, causal, scale, dtype, label):
+    T = q.shape[2]
+    flush_print(f"[gpu] {label}: fused, shape {tuple(q.shape)} {dtype} "
+                f"causal={causal}")
+    o, lse = fused(lib, q, k, v, causal, scale)
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    b = tol(dtype, T)
+    assert_close(label + " O", o.numpy(), ro, b)
+    assert_close(label + " lse", lse.numpy(), rl, b)
+    return o, ro
+
+
+# --- the fp32 single-head workloads (both paths) -------------------------------
+
+@pytest.mark.parametrize("name", ["single_head_n256_f32", "single_head_n1024_f32",
+                                  "single_head_n4096_f32"])
+def test_single_head_fp32_both_paths(gpu_lib, name):
+    w = WORKLOADS[name]
+    q, k, v = workload_qkv(w)
+    o, ro = check_full(gpu_lib, q, k, v, w.causal, w.scale, "f32", name)
+    flush_print(f"[gpu] {name}: naive")
+    no, nl = naive(gpu_lib, q, k, v, w.causal, w.scale)
+    _, rl = oracle.attention(q, k, v, w.causal, w.scale)
+    b = tol("f32", w.T)
+    assert_close(name + " naive O", no.numpy(), ro, b)
+    assert_close(name + " naive lse", nl.numpy(), rl, b)
+    assert_close(name + " fused vs naive", o.numpy(), no.numpy(), b)
+
+
+@pytest.mark.parametrize("T", [1, 100, 256, 1000])
+def test_causal_fp32_two_by_three(gpu_lib, T):
+    w = WORKLOADS[f"causal_b2h3_t{T}_f32"]
+    q, k, v = workload_qkv(w)
+    check_full(gpu_lib, q, k, v, True, w.scale, "f32", w.name)
+    flush_print(f"[gpu] {w.name}: naive")
+    no, nl = naive(gpu_lib, q, k, v, True, w.scale)
+    ro, rl = oracle.attention(q, k, v, True, w.scale)
+    assert_close(w.name + " naive O", no.numpy(), ro, tol("f32", T))
+    assert_close(w.name + " naive lse", nl.numpy(), rl, tol("f32", T))
+
+
+@pytest.mark.parametrize("T", [100, 1000])
+def test_noncausal_fp32_two_by_three(gpu_lib, T):
+    q, k, v = make_qkv(2, 3, T, D, "f32", 1200 + T)
+    check_full(gpu_lib, q, k, v, False, 0.125, "f32", f"full_b2h3_t{T}_f32")
+
+
+# --- 16-bit ragged lengths ------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 77, 128, 300, 1024])
+def test_ragged_16bit(gpu_lib, dtype, causal, T):
+    q, k, v = make_qkv(2, 3, T, D, dtype, 1300 + T)
+    check_full(gpu_lib, q, k, v, causal, 0.125, dtype,
+               f"ragged_{dtype}_c{int(causal)}_t{T}")
+
+
+@pytest.mark.parametrize("T", [77, 300])
+def test_bf16_within_twice_torch_cpu_error(gpu_lib, T):
+    """The rule of "Flash attention in PyTorch, then in Triton" (section "A
+    kernel in Triton"): our bf16 error against float64 is at most twice that
+    of torch's own attention in bf16 (here torch's CPU kernel), plus a tiny
+    margin."""
+    q, k, v = make_qkv(2, 3, T, D, "bf16", 1400 + T)
+    o, _ = fused(gpu_lib, q, k, v, True, 0.125)
+    ro, _ = oracle.attention(q, k, v, True, 0.125)
+    theirs = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=True, scale=0.125).float().numpy()
+    ours_err = np.abs(o.numpy() - ro).max()
+    their_err = np.abs(theirs - ro).max()
+    flush_print(f"    bf16 T={T}: ours {ours_err:.3e} torch-cpu {their_err:.3e}")
+    assert ours_err <= 2 * their_err + 1e-5
+
+
+# --- closed forms and stress inputs on the GPU -----------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_single_token_returns_v_exactly(gpu_lib, dtype, causal):
+    q, k, v = make_qkv(3, 5, 1, D, dtype, 1500)
+    flush_print(f"[gpu] T=1 {dtype} causal={causal}")
+    o, lse = fused(gpu_lib, q, k, v, causal, 0.125)
+    if dtype == "f32":
+        # the lone weight is exp2 of the rounding error of m*c, which cancels
+        # in o = (p v) / p up to a couple of fp32 ulps
+        np.testing.assert_allclose(o.numpy(), v.numpy(), rtol=4 * 2.0 ** -23,
+                                   atol=0)
+    else:  # ... and vanishes entirely in the 16-bit output rounding
+        assert torch.equal(o.to(v.dtype), v)
+    ro, rl = oracle.attention(q, k, v, causal, 0.125)
+    assert_close("T=1 lse", lse.numpy(), rl, tol(dtype, 1))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_query_prefix_mean(gpu_lib, dtype):
+    T = 300
+    _, k, v = make_qkv(1, 2, T, D, dtype, 1600)
+    q = torch.zeros_like(k)
+    flush_print(f"[gpu] Q=0 {dtype}")
+    o, lse = fused(gpu_lib, q, k, v, True, 0.125)
+    v64 = v.double().numpy()
+    counts = np.arange(1, T + 1, dtype=np.float64)
+    mean = np.cumsum(v64, axis=2) / counts[None, None, :, None]
+    assert_close("Q=0 O", o.numpy(), mean, tol(dtype, T))
+    assert_close("Q=0 lse", lse.numpy(),
+                 np.broadcast_to(np.log(counts), lse.shape), tol(dtype, T))
+
+
+def test_one_hot_fp32_selects_rows(gpu_lib):
+    """Query i = alpha * e_pi(i), key j = e_j: a gap of 360 in exp2 units
+    makes every other weight exactly 0 in fp32, so O_i = V_pi(i) up to the
+    couple of ulps the lone weight's exp2 rounding leaves."""
+    T = 64
+    g = np.random.Generator(np.random.PCG64(17))
+    pi = np.array([g.integers(0, i + 1) for i in range(T)])
+    kk = np.zeros((T, D), np.float32)
+    kk[np.arange(T), np.arange(T)] = 1.0
+    qq = np.zeros((T, D), np.float32)
+    qq[np.arange(T), pi] = 2000.0
+    vv = g.standard_normal((T, D)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).reshape(1, 1, T, D) for x in (qq, kk, vv))
+    flush_print("[gpu] one-hot fp32")
+    o, _ = fused(gpu_lib, q, k, v, True, 0.125)
+    np.testing.assert_allclose(o[0, 0].numpy(), vv[pi], rtol=4 * 2.0 ** -23,
+                               atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [256, 1000])
+def test_late_spike(gpu_lib, dtype, T):
+    q, k, v = late_spike_qkv(T, D, dtype)
+    check_full(gpu_lib, q, k, v, False, 0.125, dtype, f"late_spike_{dtype}_{T}")
+    check_full(gpu_lib, q, k, v, True, 0.125, dtype, f"late_spike_c_{dtype}_{T}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
+def test_scale_sign_and_zero(gpu_lib, dtype, scale):
+    q, k, v = make_qkv(1, 3, 200, D, dtype, 1700)
+    check_full(gpu_lib, q, k, v, True, scale, dtype, f"scale_{scale}_{dtype}")
+
+
+def test_lse_optional_and_stream(gpu_lib):
+    q, k, v = make_qkv(2, 2, 333, D, "bf16", 1800)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    flush_print("[gpu] lse=None on a side stream")
+    s = torch.cuda.Stream()  # default priority
+    o1 = torch.empty_like(qd)
+    with torch.cuda.stream(s):
+        gpu_lib.attn_fwd_stream(qd, kd, vd, o1, None, True, 0.125, stream=s)
+    s.synchronize()
+    o2, _ = gpu_lib.attention(qd, kd, vd, True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    o3 = torch.empty_like(qd)
+    gpu_lib.attn_fwd(qd, kd, vd, o3, None, True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o2)
+
+
+def test_invalid_calls_raise_on_gpu(gpu_lib):
+    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gpu_lib.AttnError):
+        gpu_lib.attention(q, q, q, True, 0.125)
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(gpu_lib.AttnError):
+        gpu_lib.attn_naive_fwd(q, q, q, torch.empty_like(q), None, ws, True, 0.1)
+
+
+def test_kernel_attributes(gpu_lib):
+    for i in range(gpu_lib.attn_kernel_count()):
+        a = gpu_lib.attn_kernel_attributes(i)
+        flush_print(f"    {gpu_lib.attn_kernel_name(i)}: {a}")
+        assert a["private_bytes"] == 0, "register spills"
+        assert a["workgroups_per_cu"] >= 1
+
+
+# --- the metric workload and the long contexts, on sampled rows ---------------------
+
+def check_sampled(lib, name, nrows, seed):
+    w = WORKLOADS[name]
+    flush_print(f"[gpu] {name}: generating inputs")
+    q, k, v = workload_qkv(w)
+    flush_print(f"[gpu] {name}: fused")
+    o, lse = fused(lib, q, k, v, w.causal, w.scale)
+    rows = sample_rows(w.B, w.H, w.T, nrows, seed,
+                       boundaries=(64, 128, 256, w.T // 2))
+    flush_print(f"[gpu] {name}: oracle on {len(rows)} rows")
+    ro, rl = oracle.attention(q, k, v, w.causal, w.scale, rows=rows)
+    b = tol(w.dtype, w.T)
+    assert_close(name + " O", o.reshape(-1, D).numpy()[rows], ro, b)
+    assert_close(name + " lse", lse.reshape(-1).numpy()[rows], rl, b)
+    assert np.all(np.isfinite(o.numpy())), "non-finite output somewhere"
+
+
+def test_metric_workload_sampled(gpu_lib):
+    check_sampled(gpu_lib, "gpt2s_b4h12_t8192_bf16", 4096, 4001)
+
+
+@pytest.mark.parametrize("name", ["long_b1h16_t32768_bf16",
+                                  "long_b1h16_t131072_bf16"])
+def test_long_context_sampled(gpu_lib, name):
+    check_sampled(gpu_lib, name, 4096, 5001)
+
+
+@pytest.mark.timeout(600)
+def test_metric_workload_every_row(gpu_lib):
+    """All 393216 rows of the 4 x 12 x 8192 bf16 causal workload, in chunks
+    of one (batch, head) slice so progress is visible."""
+    w = WORKLOADS["gpt2s_b4h12_t8192_bf16"]
+    q, k, v = workload_qkv(w)
+    flush_print("[gpu] metric workload, every row: fused")
+    o, lse = fused(gpu_lib, q, k, v, True, w.scale)
+    qn, kn, vn = (x.float().numpy() for x in (q, k, v))
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ro, rl = oracle.attention(qn[b, h], kn[b, h], vn[b, h], True, w.scale)
+            eo = np.abs(o[b, h].numpy().astype(np.float64) - ro).max()
+            el = np.abs(lse[b, h].numpy().astype(np.float64) - rl).max()
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        flush_print(f"    batch {b}: max|dO| so far {worst_o:.3e}, "
+                    f"max|dlse| {worst_l:.3e}")
+    assert worst_o <= tol("bf16", w.T) and worst_l <= tol("bf16", w.T)
