@@ -46,9 +46,9 @@ int check_shape(int B, int H, int T, int D) {
     return ATTN_OK;
 }
 
-// Largest 1-D grid one fused launch takes: workgroups * 256 threads must
+// Largest 1-D grid one fused launch takes: workgroups * 512 threads must
 // stay below 2^32.
-constexpr uint64_t kMaxFusedWorkgroups = (1ull << 24) - 1;
+constexpr uint64_t kMaxFusedWorkgroups = (1ull << 23) - 1;
 
 }  // namespace
 
@@ -65,7 +65,9 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return ATTN_ERR_INVALID;
     if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
-    const uint64_t nq = ((uint64_t)T + attn::kBlockM - 1) / attn::kBlockM;
+    int bm, bn;
+    attn_fused_tile(dtype, &bm, &bn);
+    const uint64_t nq = ((uint64_t)T + bm - 1) / bm;
     if (nq * (uint64_t)B * (uint64_t)H > kMaxFusedWorkgroups)
         return ATTN_ERR_UNSUPPORTED;
     // exp2 multiplier: |scale| * log2(e); a negative scale negates Q instead
@@ -160,7 +162,7 @@ int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
         const int nq = (T + bm - 1) / bm;
         uint64_t kv_rows = 0;
         for (int qt = 0; qt < nq; ++qt) {
-            const int tiles = attn::key_tiles(qt, T, bn, causal != 0);
+            const int tiles = attn::key_tiles(qt, T, bn, causal != 0, bm);
             const uint64_t rows = (uint64_t)tiles * bn;
             kv_rows += rows < (uint64_t)T ? rows : (uint64_t)T;
         }
@@ -220,7 +222,7 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);
-    const int threads = 256;
+    const int threads = attn::kThreads;
     int per_cu = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
     if (e != hipSuccess) return hip_fail(e);

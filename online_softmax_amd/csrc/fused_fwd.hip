@@ -32,6 +32,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fused_layout.h"
 #include "kernels.h"
 
@@ -94,18 +96,243 @@ __device__ inline float halves_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of the two 16-bit values packed in `pair`, added to acc in fp32
+// (v_dot2c_f32_{bf16,f16} against (1, 1)): the row sum of the rounded p.
+template <int DT>
+__device__ inline float sum2(uint32_t pair, float acc);
+template <>
+__device__ inline float sum2<ATTN_DT_BF16>(uint32_t pair, float acc) {
+    const v2bf16 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf16, pair), one,
+                                           acc, false);
+}
+template <>
+__device__ inline float sum2<ATTN_DT_F16>(uint32_t pair, float acc) {
+    const v2f16 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2f16, pair), one, acc,
+                                  false);
+}
+
+// Lazy rescaling. The online softmax may exponentiate against any reference
+// point m, as long as O, l and lse all use the same one and no weight
+// overflows. A tile whose row maximum exceeds the reference by at most
+// kLazyLog2 (in log2 units, so every weight is <= 2^kLazyLog2 = 256) is
+// exponentiated against the old reference; only a larger jump moves the
+// reference and rescales O and l by exp2(m_old - m_new). After the first
+// tile this is rare for typical scores, and the decision is wave-uniform.
+constexpr float kLazyLog2 = 8.0f;
+
+// Online-softmax state of one lane: the reference maximum m (raw score
+// units), mc = m * c, and this lane-half's running denominator l.
+struct RowState {
+    float m, mc, l;
+};
+
 // ---------------------------------------------------------------------------
 // 16-bit inputs (bf16 or f16), fp32 accumulation.
 // c = |scale| * log2(e); qsign = 0x80008000 negates Q for a negative scale.
 // ---------------------------------------------------------------------------
+
+// The online-softmax step of one tile: mask (EDGE tiles: keys >= T and,
+// causal, keys after the row), row maximum, the lazy reference update (with
+// the rescale of O and l when some row's maximum jumps by more than
+// kLazyLog2), the weights p = exp2(s*c - m*c) rounded into the P fragment,
+// and their sum into l.
+template <int DT, bool CAUSAL, bool EDGE>
+__device__ inline void softmax16(v16f32 (&s)[2], v4u32 (&pf)[4],
+                                 v16f32 (&oacc)[2], RowState& st, float c,
+                                 int k0, int T, int my_q, int hh) {
+    if (EDGE) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 32 * nt + acc_row(r, hh);
+                if (key >= T || (CAUSAL && key > my_q)) s[nt][r] = -INFINITY;
+            }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+    mx = halves_max(mx);
+    // a fully masked row has mx = -inf and never asks for a rescale
+    if (__builtin_amdgcn_ballot_w64(mx * c - st.mc > kLazyLog2) != 0) {
+        const float m_new = fmaxf(st.m, mx);
+        const float mc_new = m_new * c;
+        const float corr = fast_exp2(st.mc - mc_new);
+        st.m = m_new;
+        st.mc = mc_new;
+        st.l *= corr;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
+    }
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int nt = ks >> 1, r0 = (ks & 1) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = s[nt][r0 + 2 * i], x1 = s[nt][r0 + 2 * i + 1];
+            float p0 = fast_exp2(fmaf(x0, c, -st.mc));
+            float p1 = fast_exp2(fmaf(x1, c, -st.mc));
+            if (EDGE) {  // masked keys weigh exactly 0 (also for c = 0)
+                if (x0 == -INFINITY) p0 = 0.f;
+                if (x1 == -INFINITY) p1 = 0.f;
+            }
+            pf[ks][i] = pack2<DT>(p0, p1);
+            if (i & 1)
+                t1 = sum2<DT>(pf[ks][i], t1);
+            else
+                t0 = sum2<DT>(pf[ks][i], t0);
+        }
+    }
+    st.l += t0 + t1;
+}
+
+typedef short v4i16 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte offset lds_off + 16 * l (lds_off must be
+// wave-uniform). Issued as inline assembly so the compiler does not treat the
+// LDS write as aliasing every later LDS read and drain the load queue before
+// each tile; completion is tracked explicitly with wait_vmcnt and a barrier.
+__device__ inline void dma16(const void* gptr, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_off), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending
+// (other counters untouched).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until this wave's loads of a tile have landed, leaving `younger`
+// later tiles (4 load instructions each) in flight.
+__device__ inline void wait_tiles(int younger) {
+    if (younger >= 2)
+        wait_vmcnt<8>();
+    else if (younger == 1)
+        wait_vmcnt<4>();
+    else
+        wait_vmcnt<0>();
+}
+
+// S^T = K Q^T for one 64-key tile from a swizzled LDS K tile.
+template <int DT>
+__device__ inline void qk16(const char* __restrict__ kb, const v4u32 (&qf)[4],
+                            v16f32 (&s)[2], int lane) {
+    const int ql = lane & 31, hh = lane >> 5;
+    v4u32 kf[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kf[nt][ks] = *(const v4u32*)(kb + kfrag_byte(ql, hh, nt, ks));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s[nt] = mfma16<DT>(kf[nt][ks], qf[ks], s[nt]);
+    }
+}
+
+// V^T fragments of one 64-key tile, by transposed LDS reads.
+__device__ inline void vfrag16(const char* __restrict__ vb, v4u32 (&vf)[2][4],
+                               int lane) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(vb + vtr_byte(lane, mt, ks, 0)));
+            const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(vb + vtr_byte(lane, mt, ks, 1)));
+            const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
+            vf[mt][ks] = (v4u32){a2[0], a2[1], b2[0], b2[1]};
+        }
+}
+
+// O^T += V^T P^T.
+template <int DT>
+__device__ inline void pv16(const v4u32 (&vf)[2][4], const v4u32 (&pf)[4],
+                            v16f32 (&oacc)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            oacc[mt] = mfma16<DT>(vf[mt][ks], pf[ks], oacc[mt]);
+}
+
+// Row maximum of an unmasked S^T tile and the lazy reference update.
+__device__ inline void lazy_update(const v16f32 (&s)[2], v16f32 (&oacc)[2],
+                                   RowState& st, float c) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+    mx = halves_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx * c - st.mc > kLazyLog2) != 0) {
+        const float m_new = fmaxf(st.m, mx);
+        const float mc_new = m_new * c;
+        const float corr = fast_exp2(st.mc - mc_new);
+        st.m = m_new;
+        st.mc = mc_new;
+        st.l *= corr;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
+    }
+}
+
+// Weights of a main tile against the current reference (no mask, no max):
+// p = exp2(s*c - m*c) rounded into the P fragment, and their sum into l.
+template <int DT>
+__device__ inline void weights16(const v16f32 (&s)[2], v4u32 (&pf)[4],
+                                 RowState& st, float c) {
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int nt = ks >> 1, r0 = (ks & 1) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p0 = fast_exp2(fmaf(s[nt][r0 + 2 * i], c, -st.mc));
+            const float p1 = fast_exp2(fmaf(s[nt][r0 + 2 * i + 1], c, -st.mc));
+            pf[ks][i] = pack2<DT>(p0, p1);
+            if (i & 1)
+                t1 = sum2<DT>(pf[ks][i], t1);
+            else
+                t0 = sum2<DT>(pf[ks][i], t0);
+        }
+    }
+    st.l += t0 + t1;
+}
+
+// 4 waves, 32 query rows each. Main tiles (no mask) run software-pipelined:
+// iteration j computes S(j+1) = K(j+1) Q^T in the same block as the weights
+// of tile j and O += V(j) P(j), so a wave always has independent matrix and
+// vector work in flight; the (at most two) edge tiles run one at a time with
+// masks. K and V tiles arrive by direct global -> LDS loads three tiles ahead
+// into a 4-stage ring (schedule in fused_layout.h).
 template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
     constexpr int BN = kBlockN16;
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKTile16];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kVTile16];
+    __shared__ __attribute__((aligned(1024))) char ring[kStages][2][kTileBytes16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -122,6 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     const int wq0 = qt * kBlockM + 32 * wave;  // first query row of this wave
     const int my_q = wq0 + ql;                 // this lane's query row
     const int n_tiles = key_tiles(qt, T, BN, CAUSAL);
+    const int n_main = main_tiles(qt, T, BN, CAUSAL);
 
     v4u32 qf[4];
 #pragma unroll
@@ -131,139 +359,94 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
             x = *(const v4u32*)(qh + (int64_t)my_q * kHeadDim + q_col16(hh, ks));
         qf[ks] = x ^ qsign;
     }
+    wait_vmcnt<0>();  // Q is in registers before the ring loads start
 
-    v4u32 kr[2], vr[2];
-    auto gload = [&](int kt) {
-        const int k0 = kt * BN;
+    // Direct loads of tile t (K and V) into ring stage t % kStages: 4 wave
+    // instructions, 16 bytes per lane. Rows past T fetch row T-1 instead (a
+    // finite value whose weight the edge mask sets to 0).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
+    int krow[2], kcol[2], vrow[2], vcol[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        dl_src(wave, i, lane, false, &krow[i], &kcol[i]);
+        dl_src(wave, i, lane, true, &vrow[i], &vcol[i]);
+    }
+    auto issue = [&](int t) {
+        const int k0 = t * BN;
+        const uint32_t stage_off =
+            (uint32_t)(uintptr_t)(lds_void*)ring[t % kStages][0];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            int row, col;
-            k_stage16(tid, i, &row, &col);
-            v4u32 x = {0u, 0u, 0u, 0u};
-            if (k0 + row < T)
-                x = *(const v4u32*)(kh + (int64_t)(k0 + row) * kHeadDim + col);
-            kr[i] = x;
-        }
-        int key0, dim0;
-        v_stage16(tid, &key0, &dim0);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            v4u32 x = {0u, 0u, 0u, 0u};
-            if (k0 + key0 + e < T)
-                x = *(const v4u32*)(vh + (int64_t)(k0 + key0 + e) * kHeadDim +
-                                    dim0);
-            vr[e] = x;
+            const int rk = min(k0 + krow[i], T - 1);
+            const int rv = min(k0 + vrow[i], T - 1);
+            dma16(kh + (int64_t)rk * kHeadDim + 8 * kcol[i],
+                  stage_off + 1024 * (2 * wave_u + i));
+            dma16(vh + (int64_t)rv * kHeadDim + 8 * vcol[i],
+                  stage_off + kTileBytes16 + 1024 * (2 * wave_u + i));
         }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int row, col;
-            k_stage16(tid, i, &row, &col);
-            *(v4u32*)&sk[buf][k_lds16(row, col)] = kr[i];
-        }
-        int key0, dim0;
-        v_stage16(tid, &key0, &dim0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t a = vr[0][j], b = vr[1][j];
-            // dims dim0 + 2j and dim0 + 2j + 1, each as (key0, key0 + 1)
-            *(uint32_t*)&sv[buf][v_lds16(dim0 + 2 * j, key0)] =
-                (a & 0xffffu) | (b << 16);
-            *(uint32_t*)&sv[buf][v_lds16(dim0 + 2 * j + 1, key0)] =
-                (a >> 16) | (b & 0xffff0000u);
-        }
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
 
     v16f32 oacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
-    float m = -FLT_MAX;  // running max of raw scores (finite start: no inf-inf)
-    float l = 0.f;       // running denominator, this lane-half's keys only
+    // reference max starts finite (-FLT_MAX): no inf - inf, and scale 0 works
+    RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
 
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < n_tiles;
-        if (more) gload(kt + 1);
-        const int k0 = kt * BN;
-        // a wave skips tiles none of its rows can see (still joins barriers)
-        if (!CAUSAL || k0 <= wq0 + 31) {
-            v16f32 s[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    s[nt] = mfma16<DT>(
-                        *(const v4u32*)&sk[buf][kfrag16(ql, hh, nt, ks)],
-                        qf[ks], s[nt]);
-            }
-            const bool edge =
-                (CAUSAL && k0 + BN - 1 > wq0) || (k0 + BN > T);
-            if (edge) {
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * nt + acc_row(r, hh);
-                        if (key >= T || (CAUSAL && key > my_q))
-                            s[nt][r] = -INFINITY;
-                    }
-            }
-            float mx = s[0][0];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
-            mx = halves_max(mx);
-            const float m_new = fmaxf(m, mx);
-            const float mc = m_new * c;
-            const float corr = fast_exp2(m * c - mc);
-            m = m_new;
-            float rs = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[nt][r], c, -mc));
-                    if (edge && s[nt][r] == -INFINITY) p = 0.f;
-                    s[nt][r] = p;
-                    rs += p;
-                }
-            l = l * corr + rs;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
-            v4u32 pf[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int nt = ks >> 1, r0 = (ks & 1) * 8;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pf[ks][i] =
-                        pack2<DT>(s[nt][r0 + 2 * i], s[nt][r0 + 2 * i + 1]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    oacc[mt] = mfma16<DT>(
-                        *(const v4u32*)&sv[buf][vfrag16(ql, hh, mt, ks)],
-                        pf[ks], oacc[mt]);
-        }
-        if (more) lstore(buf ^ 1);
+    for (int t = 0; t < 3 && t < n_tiles; ++t) issue(t);
+
+    // Main iteration j: S(j) is in scur with its reference update done.
+    auto main_iter = [&](int j, v16f32(&scur)[2], v16f32(&snext)[2],
+                         auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        if (NEXT) wait_tiles(ring_younger(n_tiles, j, j + 1));
         __syncthreads();
+        if (j + 3 < n_tiles) issue(j + 3);
+        v4u32 vf[2][4], pf[4];
+        vfrag16(ring[j % kStages][1], vf, lane);
+        weights16<DT>(scur, pf, st, c);
+        if (NEXT) qk16<DT>(ring[(j + 1) % kStages][0], qf, snext, lane);
+        pv16<DT>(vf, pf, oacc);
+        if (NEXT) lazy_update(snext, oacc, st, c);
+    };
+
+    if (n_main > 0) {
+        v16f32 sa[2], sb[2];
+        wait_tiles(ring_younger(n_tiles, 0, 0));
+        __syncthreads();
+        qk16<DT>(ring[0][0], qf, sa, lane);
+        lazy_update(sa, oacc, st, c);
+        using Y = std::integral_constant<bool, true>;
+        using N = std::integral_constant<bool, false>;
+        int j = 0;
+        for (; j + 2 < n_main; j += 2) {  // unrolled: S(j) ping-pongs sa/sb
+            main_iter(j, sa, sb, Y());
+            main_iter(j + 1, sb, sa, Y());
+        }
+        if (j + 1 < n_main) {
+            main_iter(j, sa, sb, Y());
+            main_iter(j + 1, sb, sa, N());
+        } else {
+            main_iter(j, sa, sb, N());
+        }
+    }
+    // edge tiles (diagonal or ragged; at most two), one at a time
+    for (int t = n_main; t < n_tiles; ++t) {
+        wait_tiles(ring_younger(n_tiles, t, t));
+        __syncthreads();
+        if (t + 3 < n_tiles) issue(t + 3);
+        if (!CAUSAL || t * BN <= wq0 + 31) {  // a wave skips tiles it cannot see
+            v16f32 s[2];
+            v4u32 vf[2][4], pf[4];
+            qk16<DT>(ring[t % kStages][0], qf, s, lane);
+            vfrag16(ring[t % kStages][1], vf, lane);
+            softmax16<DT, CAUSAL, true>(s, pf, oacc, st, c, t * BN, T, my_q, hh);
+            pv16<DT>(vf, pf, oacc);
+        }
     }
 
-    const float lt = halves_sum(l);
+    const float lt = halves_sum(st.l);
     const float inv = 1.0f / lt;
     if (my_q < T) {
         uint16_t* orow = o + base + (int64_t)my_q * kHeadDim;
@@ -278,14 +461,78 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
                 *(v2u32*)(orow + 32 * mt + acc_row(4 * g, hh)) = w;
             }
         if (lse != nullptr && hh == 0)
-            lse[(int64_t)bh * T + my_q] = (m * c + log2f(lt)) * kLn2;
+            lse[(int64_t)bh * T + my_q] = (st.mc + log2f(lt)) * kLn2;
     }
 }
 
 // ---------------------------------------------------------------------------
-// fp32 inputs: the same schedule on v_mfma_f32_32x32x2_f32, 32-key tiles.
+// fp32 inputs: the same schedule on v_mfma_f32_32x32x2_f32, 32-key tiles,
+// fp32 weights (no lazy path: this kernel is bound by the fp32 matrix rate).
 // qsign = 0x80000000 negates Q for a negative scale.
 // ---------------------------------------------------------------------------
+template <bool CAUSAL, bool EDGE>
+__device__ inline void tile32(const float* __restrict__ skb,
+                              const float* __restrict__ svb,
+                              const v4f32 (&qf)[8], v16f32 (&oacc)[2],
+                              RowState& st, float c, int k0, int T, int my_q,
+                              int ql, int hh) {
+    v16f32 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const v4f32 kf = *(const v4f32*)&skb[kfrag32(ql, hh, g)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[i], qf[g][i], s, 0, 0,
+                                                      0);
+    }
+    if (EDGE) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + acc_row(r, hh);
+            if (key >= T || (CAUSAL && key > my_q)) s[r] = -INFINITY;
+        }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = halves_max(mx);
+    const float m_new = fmaxf(st.m, mx);
+    const float mc_new = m_new * c;
+    const float corr = fast_exp2(st.mc - mc_new);
+    st.m = m_new;
+    st.mc = mc_new;
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], c, -mc_new));
+        if (EDGE && s[r] == -INFINITY) p = 0.f;
+        s[r] = p;
+        if (r & 1)
+            t1 += p;
+        else
+            t0 += p;
+    }
+    st.l = st.l * corr + (t0 + t1);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
+    // O^T += V^T P^T: step 4g + i pairs key 8g + 4h + i of each half with
+    // accumulator register 4g + i of the score tile.
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const v4f32 vf = *(const v4f32*)&svb[vfrag32(ql, hh, mt, g)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    vf[i], s[4 * g + i], oacc[mt], 0, 0, 0);
+        }
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
     const float* __restrict__ q, const float* __restrict__ k,
@@ -310,6 +557,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
     const int wq0 = qt * kBlockM + 32 * wave;
     const int my_q = wq0 + ql;
     const int n_tiles = key_tiles(qt, T, BN, CAUSAL);
+    const int n_main = main_tiles(qt, T, BN, CAUSAL);
 
     v4f32 qf[8];
 #pragma unroll
@@ -370,75 +618,25 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
-    float m = -FLT_MAX;
-    float l = 0.f;
+    RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
 
-    for (int kt = 0; kt < n_tiles; ++kt) {
+    auto step = [&](int kt, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
         const int buf = kt & 1;
         const bool more = kt + 1 < n_tiles;
         if (more) gload(kt + 1);
         const int k0 = kt * BN;
-        if (!CAUSAL || k0 <= wq0 + 31) {
-            v16f32 s;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const v4f32 kf = *(const v4f32*)&sk[buf][kfrag32(ql, hh, g)];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[i], qf[g][i], s,
-                                                              0, 0, 0);
-            }
-            const bool edge =
-                (CAUSAL && k0 + BN - 1 > wq0) || (k0 + BN > T);
-            if (edge) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + acc_row(r, hh);
-                    if (key >= T || (CAUSAL && key > my_q)) s[r] = -INFINITY;
-                }
-            }
-            float mx = s[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = halves_max(mx);
-            const float m_new = fmaxf(m, mx);
-            const float mc = m_new * c;
-            const float corr = fast_exp2(m * c - mc);
-            m = m_new;
-            float rs = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[r], c, -mc));
-                if (edge && s[r] == -INFINITY) p = 0.f;
-                s[r] = p;
-                rs += p;
-            }
-            l = l * corr + rs;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
-            // O^T += V^T P^T: step 4g + i pairs key 8g + 4h + i of each half
-            // with accumulator register 4g + i of the score tile.
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const v4f32 vf =
-                        *(const v4f32*)&sv[buf][vfrag32(ql, hh, mt, g)];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            vf[i], s[4 * g + i], oacc[mt], 0, 0, 0);
-                }
-        }
+        if (!EDGE || !CAUSAL || k0 <= wq0 + 31)
+            tile32<CAUSAL, EDGE>(sk[buf], sv[buf], qf, oacc, st, c, k0, T, my_q,
+                                 ql, hh);
         if (more) lstore(buf ^ 1);
         __syncthreads();
-    }
+    };
+    int kt = 0;
+    for (; kt < n_main; ++kt) step(kt, std::integral_constant<bool, false>());
+    for (; kt < n_tiles; ++kt) step(kt, std::integral_constant<bool, true>());
 
-    const float lt = halves_sum(l);
+    const float lt = halves_sum(st.l);
     const float inv = 1.0f / lt;
     if (my_q < T) {
         float* orow = o + base + (int64_t)my_q * kHeadDim;
@@ -452,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
                 *(v4f32*)(orow + 32 * mt + acc_row(4 * g, hh)) = w;
             }
         if (lse != nullptr && hh == 0)
-            lse[(int64_t)bh * T + my_q] = (m * c + log2f(lt)) * kLn2;
+            lse[(int64_t)bh * T + my_q] = (st.mc + log2f(lt)) * kLn2;
     }
 }
 
@@ -462,16 +660,19 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
 hipError_t launch_fused(const void* q, const void* k, const void* v, void* o,
                         float* lse, int BH, int T, int causal, float c,
                         bool negate_q, int dt, hipStream_t stream) {
-    const int nq = (T + kBlockM - 1) / kBlockM;
-    const dim3 grid((unsigned)(nq * BH));
-    const dim3 block(kThreads);
     if (dt == ATTN_DT_F32) {
+        const int nq = (T + kBlockM - 1) / kBlockM;
+        const dim3 grid((unsigned)(nq * BH));
+        const dim3 block(kThreads);
         const uint32_t sign = negate_q ? 0x80000000u : 0u;
         auto fn = causal ? fused_fwd32<true> : fused_fwd32<false>;
         hipLaunchKernelGGL(fn, grid, block, 0, stream, (const float*)q,
                            (const float*)k, (const float*)v, (float*)o, lse, T,
                            nq, c, sign);
     } else {
+        const int nq = (T + kBlockM - 1) / kBlockM;
+        const dim3 grid((unsigned)(nq * BH));
+        const dim3 block(kThreads);
         const uint32_t sign = negate_q ? 0x80008000u : 0u;
         if (dt == ATTN_DT_BF16) {
             auto fn = causal ? fused_fwd16<ATTN_DT_BF16, true>

@@ -94,15 +94,107 @@ ATTN_HD void tile_of(int block, int total, int nq, bool causal, int* bh,
     *qt = causal ? nq - 1 - t : t;
 }
 
-// Number of key tiles of `bn` keys query tile qt reads: every tile that
-// holds a key visible to one of its valid rows (rows < T).
-ATTN_HD int key_tiles(int qt, int T, int bn, bool causal) {
+// Number of key tiles of `bn` keys query tile qt (of bm rows) reads: every
+// tile that holds a key visible to one of its valid rows (rows < T).
+ATTN_HD int key_tiles(int qt, int T, int bn, bool causal, int bm = kBlockM) {
     const int all = (T + bn - 1) / bn;
     if (!causal) return all;
-    int last = qt * kBlockM + kBlockM - 1;
+    int last = qt * bm + bm - 1;
     if (last > T - 1) last = T - 1;
     const int n = last / bn + 1;
     return n < all ? n : all;
+}
+
+// Number of leading key tiles that need no mask for any row of query tile
+// qt: every key of the tile is < T and (causal) <= the tile's first row.
+// Tiles from here to key_tiles() are the edge tiles (diagonal or ragged).
+ATTN_HD int main_tiles(int qt, int T, int bn, bool causal, int bm = kBlockM) {
+    int n = T / bn;  // tiles wholly below T
+    if (causal) {
+        const int c = (qt * bm + 1) / bn;  // tiles with k0 + bn - 1 <= q0
+        if (c < n) n = c;
+    }
+    const int all = key_tiles(qt, T, bn, causal, bm);
+    return n < all ? n : all;
+}
+
+// ---- 16-bit ping-pong schedule ----------------------------------------------
+// 8 waves, two groups of 4 (wave w is in group w / 4; SIMD s runs waves s and
+// s + 4). Each wave owns 32 query rows: 256 per workgroup. Tile j of a wave
+// is an MFMA phase (O += V(j-1) P(j-1), then S(j) = K(j) Q^T) followed by a
+// VALU phase (the softmax of S(j)); group g runs phase r = p - g of its own
+// sequence at workgroup phase p, so on every SIMD one wave's products overlap
+// the other wave's softmax. Phases end with a workgroup barrier.
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPBlockM = 32 * kPPWaves;
+// Workgroup phases for n key tiles: group 1's last MFMA phase is 2n + 1.
+ATTN_HD int pp_phases(int n) { return 2 * n + 2; }
+// Staging of tile i: at the start of phase 2i, group 0 issues the global
+// loads of K(i+1) and group 1 those of V(i); at the end of phase 2i+1 they
+// are written to LDS, K(i+1) into K buffer (i+1)&1 and V(i) into V buffer
+// i&1. K(i) is read in phases 2i and 2i+1, V(i) in phases 2i+2 and 2i+3.
+ATTN_HD int pp_k_tile_loaded(int p) { return p / 2 + 1; }   // p even
+ATTN_HD int pp_v_tile_loaded(int p) { return p / 2; }       // p even
+
+// ---- 16-bit direct-to-LDS staging ---------------------------------------------
+// K and V tiles (64 keys x 64 dims, 128-byte rows, no padding) are written by
+// global_load_lds_dwordx4: lane l of a wave instruction lands its 16 bytes at
+// LDS base + 16*l, so a wave instruction fills 8 consecutive rows and each
+// lane fetches whichever global 16-byte chunk belongs in its slot. Chunks are
+// XOR-swizzled within a row so the fragment reads hit distinct banks:
+//   K: chunk c of row r sits at slot c ^ ((r >> 1) & 7)   (16-byte reads by
+//      16 consecutive rows at one chunk),
+//   V: chunk c of row r sits at slot c ^ ((r & 2) << 1)   (8-byte transposed
+//      reads of 4 consecutive rows x 4 chunks per 16 lanes).
+constexpr int kStages = 4;                 // LDS ring depth (tiles resident + in flight)
+constexpr int kTileBytes16 = kBlockN16 * kHeadDim * 2;   // 8 KiB per K or V tile
+ATTN_HD int swz_k(int row) { return (row >> 1) & 7; }
+ATTN_HD int swz_v(int row) { return (row & 2) << 1; }
+// Byte offset of (row, 16-byte chunk) of a K tile / of element (row, d) of a
+// V tile inside their 8 KiB tiles.
+ATTN_HD int k_byte(int row, int chunk) { return row * 128 + ((chunk ^ swz_k(row)) << 4); }
+ATTN_HD int v_byte(int row, int d) {
+    return row * 128 + (((d >> 3) ^ swz_v(row)) << 4) + ((d & 7) << 1);
+}
+// Direct load: wave w's instruction i (0, 1) of a tile, lane l: the tile row
+// and logical chunk this lane fetches (it lands at byte 1024*(2w+i) + 16*l).
+ATTN_HD void dl_src(int w, int i, int l, bool is_v, int* row, int* chunk) {
+    const int slot = (2 * w + i) * 64 + l;
+    *row = slot >> 3;
+    *chunk = (slot & 7) ^ (is_v ? swz_v(*row) : swz_k(*row));
+}
+// Ring schedule of the 16-bit kernel (n tiles; tile t lives in stage t % 4).
+// Tiles 0..2 are issued before the loop; iteration u (after its barrier)
+// issues tile u + 3. A main iteration j needs tile j+1 (for S(j+1)) and tile
+// j (V, waited for one iteration earlier); an edge iteration t needs tile t.
+// Before its barrier an iteration waits until the tile it needs has landed:
+// the younger tiles this wave may leave in flight number
+ATTN_HD int ring_younger(int n, int u, int needed) {
+    const int issued = (u + 2 < n - 1) ? u + 2 : n - 1;  // highest tile issued
+    return issued - needed;
+}
+// (4 load instructions per tile and wave). The stage that iteration u
+// reloads, (u + 3) % 4 = (u - 1) % 4, held tile u - 1, whose last reader is
+// iteration u - 1 (V of a main tile, or an edge tile), which every wave has
+// finished at iteration u's barrier.
+
+// K fragment of S^T tile nt, step ks for lane (ql, h): 16 bytes, dims
+// 16ks + 8h .. +7 of key 32nt + ql.
+ATTN_HD int kfrag_byte(int ql, int h, int nt, int ks) {
+    return k_byte(32 * nt + ql, 2 * ks + h);
+}
+// V^T fragment for the O^T tile mt, step ks, from two ds_read_b64_tr_b16
+// (half 0: slots 0-3, half 1: slots 4-7). Within each 16-lane group the
+// transposed read hands lane i element (i % 4) of the 8-byte chunks read by
+// lanes 4r + i/4, r = 0..3. So lane l addresses row 16ks + 8*half + 4h + r,
+// dims d0 + 4c .. +3 (r = (l%16)/4, c = l%4, d0 = 32mt + 16((l/16)%2),
+// h = l/32), and receives V[16ks + 8*half + 4h + 0..3][32mt + l%32]: the keys
+// the P fragment holds in those slots, at its head dimension.
+ATTN_HD int vtr_byte(int l, int mt, int ks, int half) {
+    const int j = l & 15, r = j >> 2, c = j & 3;
+    const int g = (l >> 4) & 1, h = l >> 5;
+    return v_byte(16 * ks + 8 * half + 4 * h + r, 32 * mt + 16 * g + 4 * c);
 }
 
 // ---- 16-bit staging: global -> registers -> LDS ---------------------------

@@ -42,6 +42,25 @@ static void check_tile_map(int BH, int T, bool causal) {
     for (int i = 0; i < total; ++i) CHECK(seen[i] == 1, "tile %d hit %d times", i, seen[i]);
 }
 
+static void check_tile_map_bm(int BH, int T, bool causal) {
+    const int nq = (T + kPPBlockM - 1) / kPPBlockM;
+    const int total = nq * BH;
+    std::vector<int> seen((size_t)total, 0);
+    for (int b = 0; b < total; ++b) {
+        int bh, qt;
+        tile_of(b, total, nq, causal, &bh, &qt);
+        CHECK(bh >= 0 && bh < BH && qt >= 0 && qt < nq, "tile_of(%d) out of range", b);
+        if (bh >= 0 && bh < BH && qt >= 0 && qt < nq) seen[(size_t)bh * nq + qt]++;
+        // every K/V row a workgroup loads is inside its slice
+        const int n = key_tiles(qt, T, kBlockN16, causal, kPPBlockM);
+        CHECK(n >= 1 && (long)(n - 1) * kBlockN16 < T, "bm256 key tiles");
+        int last = qt * kPPBlockM + kPPBlockM - 1;
+        if (last > T - 1) last = T - 1;
+        CHECK((long)n * kBlockN16 > (causal ? last : T - 1), "bm256 key cover");
+    }
+    for (int i = 0; i < total; ++i) CHECK(seen[i] == 1, "tile %d hit %d times", i, seen[i]);
+}
+
 static void check_key_cover(int T, int bn, bool causal) {
     const int nq = (T + kBlockM - 1) / kBlockM;
     for (int qt = 0; qt < nq; ++qt) {
@@ -53,6 +72,24 @@ static void check_key_cover(int T, int bn, bool causal) {
         CHECK((long)n * bn > need, "qt %d: %d tiles miss key %d", qt, n, need);
         CHECK((long)(n - 1) * bn <= need, "qt %d: tile %d sees nothing", qt, n - 1);
         CHECK((long)(n - 1) * bn < T, "qt %d: tile past T", qt);
+        const int nm = main_tiles(qt, T, bn, causal);
+        CHECK(nm >= 0 && nm <= n, "qt %d: main tiles %d of %d", qt, nm, n);
+        // the pipelined 16-bit loop stages K two tiles ahead: edge tiles
+        // (which stage only V) must be the last two at most
+        if (bn == kBlockN16) CHECK(n - nm <= 2, "qt %d: %d edge tiles", qt, n - nm);
+        for (int kt = 0; kt < nm; ++kt) {  // a main tile needs no mask at all
+            CHECK((long)kt * bn + bn <= T, "qt %d: main tile %d ragged", qt, kt);
+            if (causal)
+                CHECK((long)kt * bn + bn - 1 <= (long)qt * kBlockM,
+                      "qt %d: main tile %d crosses the diagonal", qt, kt);
+        }
+        // the first edge tile does need a mask for some row (or is ragged)
+        if (nm < n) {
+            const long k0 = (long)nm * bn;
+            const bool ragged = k0 + bn > T;
+            const bool diag = causal && k0 + bn - 1 > (long)qt * kBlockM;
+            CHECK(ragged || diag, "qt %d: tile %d is edge without a reason", qt, nm);
+        }
     }
 }
 
@@ -231,7 +268,203 @@ static void check32(int BH, int T, bool causal) {
     }
 }
 
+// The 16-bit ping-pong schedule: simulate every phase of a launch and check
+// that each LDS read finds the tile it expects, written in an earlier phase,
+// and that no buffer is rewritten in a phase in which any wave still reads it
+// (a fast wave writes at the end of a phase while slow ones may still read).
+static void check_pingpong(int T, bool causal) {
+    const int nq = (T + kPPBlockM - 1) / kPPBlockM;
+    for (int qt = 0; qt < nq; ++qt) {
+        const int n = key_tiles(qt, T, kBlockN16, causal, kPPBlockM);
+        int kbuf[2] = {-1, -1}, vbuf[2] = {-1, -1};
+        kbuf[0] = 0;  // prologue
+        const int P = pp_phases(n);
+        for (int p = 0; p < P; ++p) {
+            bool kread[2] = {false, false}, vread[2] = {false, false};
+            for (int g = 0; g < 2; ++g) {
+                const int r = p - g;
+                if (r < 0 || (r & 1)) continue;  // only MFMA phases read LDS
+                const int i = r >> 1;
+                if (i >= 1 && i - 1 < n) {
+                    CHECK(vbuf[(i - 1) & 1] == i - 1, "qt %d p %d: V(%d) missing", qt, p, i - 1);
+                    vread[(i - 1) & 1] = true;
+                }
+                if (i < n) {
+                    CHECK(kbuf[i & 1] == i, "qt %d p %d: K(%d) missing (buf holds %d)", qt, p, i, kbuf[i & 1]);
+                    kread[i & 1] = true;
+                }
+            }
+            if (p & 1) {  // end of an odd phase: K(p/2 + 1), V(p/2) land
+                const int tk = pp_k_tile_loaded(p & ~1), tv = pp_v_tile_loaded(p & ~1);
+                if (tk < n) {
+                    CHECK(!kread[tk & 1], "qt %d p %d: K buffer %d rewritten while read", qt, p, tk & 1);
+                    kbuf[tk & 1] = tk;
+                }
+                if (tv < n) {
+                    CHECK(!vread[tv & 1], "qt %d p %d: V buffer %d rewritten while read", qt, p, tv & 1);
+                    vbuf[tv & 1] = tv;
+                }
+            }
+        }
+        // every tile's PV ran: the last MFMA phase of group 1 is P - 1
+        CHECK(((P - 1 - 1) >> 1) == n, "qt %d: schedule too short", qt);
+    }
+}
+
+// Direct-load staging and fragment reads of the 16-bit kernel: every chunk of
+// a tile is fetched exactly once per stage; K fragments decode to the rows and
+// dims they claim; the transposed V reads, simulated with the hardware rule
+// (within 16 lanes, lane i receives element i%4 of the chunks of lanes
+// 4r + i/4), hand every lane and slot the key the P fragment holds there at
+// the lane's head dimension; and 16 consecutive-lane groups hit distinct
+// 4-byte banks (64 banks).
+static void decode_k(int byte, int* row, int* dim) {
+    *row = byte / 128;
+    const int slot = (byte % 128) / 16;
+    *dim = ((slot ^ swz_k(*row)) * 8) + (byte % 16) / 2;
+}
+static void decode_v(int byte, int* row, int* dim) {
+    *row = byte / 128;
+    const int slot = (byte % 128) / 16;
+    *dim = ((slot ^ swz_v(*row)) * 8) + (byte % 16) / 2;
+}
+static void check_direct16() {
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        std::vector<int> cov(64 * 8, 0);
+        for (int w = 0; w < kWaves; ++w)
+            for (int i = 0; i < 2; ++i)
+                for (int l = 0; l < 64; ++l) {
+                    int row, chunk;
+                    dl_src(w, i, l, is_v, &row, &chunk);
+                    CHECK(row >= 0 && row < 64 && chunk >= 0 && chunk < 8, "dl_src range");
+                    const int dst = 1024 * (2 * w + i) + 16 * l;
+                    const int want = is_v ? v_byte(row, 8 * chunk) : k_byte(row, chunk);
+                    CHECK(dst == want, "direct load lands at the wrong slot");
+                    cov[row * 8 + chunk]++;
+                }
+        for (int x = 0; x < 64 * 8; ++x) CHECK(cov[x] == 1, "tile chunk fetched %d times", cov[x]);
+    }
+    for (int nt = 0; nt < 2; ++nt)
+        for (int ks = 0; ks < 4; ++ks) {
+            std::vector<int> bank_use(64, 0);
+            for (int l = 0; l < 64; ++l) {
+                const int ql = l & 31, h = l >> 5;
+                const int b = kfrag_byte(ql, h, nt, ks);
+                CHECK(b % 16 == 0 && b + 16 <= kTileBytes16, "kfrag range");
+                int row, dim;
+                decode_k(b, &row, &dim);
+                CHECK(row == 32 * nt + ql && dim == 16 * ks + 8 * h, "K fragment decode");
+            }
+            for (int grp = 0; grp < 4; ++grp) {  // 16 lanes x 16 B = 256 B per cycle
+                std::vector<int> used(64, 0);
+                for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+                    const int b = kfrag_byte(l & 31, l >> 5, nt, ks);
+                    for (int x = 0; x < 4; ++x) used[(b / 4 + x) % 64]++;
+                }
+                for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "K read bank conflict");
+            }
+        }
+    for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < 4; ++ks)
+            for (int half = 0; half < 2; ++half) {
+                int addr[64];
+                for (int l = 0; l < 64; ++l) {
+                    addr[l] = vtr_byte(l, mt, ks, half);
+                    CHECK(addr[l] % 8 == 0 && addr[l] + 8 <= kTileBytes16, "vtr range");
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int g0 = l & ~15, i = l & 15;
+                    const int ql = l & 31, h = l >> 5;
+                    for (int r = 0; r < 4; ++r) {
+                        const int src = g0 + 4 * r + i / 4;
+                        int row, dim;
+                        decode_v(addr[src] + 2 * (i % 4), &row, &dim);
+                        const int slot = 4 * half + r;
+                        // key of P slot `slot` at step ks, lane-half h
+                        const int nt = ks >> 1, reg = (ks & 1) * 8 + slot;
+                        const int pkey = 32 * nt + acc_row(reg, h);
+                        CHECK(row == pkey && dim == 32 * mt + ql,
+                              "V tr lane %d slot %d: row %d dim %d, want %d %d", l, slot, row,
+                              dim, pkey, 32 * mt + ql);
+                    }
+                }
+                for (int half32 = 0; half32 < 2; ++half32) {  // 32 lanes x 8 B per cycle
+                    std::vector<int> used(64, 0);
+                    for (int l = 32 * half32; l < 32 * half32 + 32; ++l)
+                        for (int x = 0; x < 2; ++x) used[(addr[l] / 4 + x) % 64]++;
+                    for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "V tr read bank conflict");
+                }
+            }
+}
+
+// The 4-stage ring: simulate per-wave issue order and vmcnt waits, check
+// each iteration reads tiles that have landed (given the wait) and that no
+// stage is reloaded while any wave may still read it.
+static void check_ring(int n, int n_main) {
+    // loads issued per tile, in order; a wait "younger y" completes every
+    // tile except the y most recent ones issued
+    std::vector<int> stage_tile(kStages, -1);
+    std::vector<int> landed(n, 0);
+    int issued = -1;
+    auto issue = [&](int t) {
+        CHECK(t == issued + 1, "ring: tiles issued out of order");
+        issued = t;
+        stage_tile[t % kStages] = t;
+    };
+    auto wait = [&](int younger) {
+        CHECK(younger >= 0 && younger <= 2, "ring: younger %d", younger);
+        for (int t = 0; t <= issued - younger; ++t) landed[t] = 1;
+    };
+    for (int t = 0; t < 3 && t < n; ++t) issue(t);
+    // prologue S(0) (when tile 0 is a main tile)
+    if (n_main > 0) {
+        wait(ring_younger(n, 0, 0));
+        CHECK(landed[0] && stage_tile[0] == 0, "ring: prologue tile 0");
+    }
+    // last readers of each stage, as iteration indices
+    std::vector<int> k_read_at(n, -1), v_read_at(n, -1);
+    for (int u = 0; u < n; ++u) {
+        const bool main = u < n_main;
+        const int needed = main ? u + 1 : u;
+        if (main && u + 1 >= n_main) {
+            // last main iteration: no S(u+1); tile u was waited for before
+        } else {
+            wait(ring_younger(n, u, needed));
+            CHECK(needed < n && landed[needed], "ring: tile %d not landed at iteration %d", needed, u);
+        }
+        // barrier: all waves finished iteration u - 1
+        if (u + 3 < n) {
+            const int old = stage_tile[(u + 3) % kStages];
+            if (old >= 0) {
+                CHECK(k_read_at[old] < u && v_read_at[old] < u,
+                      "ring: stage of tile %d reloaded at %d, read at %d/%d", old, u,
+                      k_read_at[old], v_read_at[old]);
+            }
+            issue(u + 3);
+        }
+        if (main) {
+            if (u + 1 < n_main) {
+                CHECK(stage_tile[(u + 1) % kStages] == u + 1 && landed[u + 1], "ring: K(%d)", u + 1);
+                k_read_at[u + 1] = u;
+            }
+            CHECK(stage_tile[u % kStages] == u && landed[u], "ring: V(%d)", u);
+            v_read_at[u] = u;
+            if (u == 0) k_read_at[0] = -1;
+        } else {
+            CHECK(stage_tile[u % kStages] == u && landed[u], "ring: edge tile %d", u);
+            k_read_at[u] = v_read_at[u] = u;
+        }
+    }
+}
+
 int main() {
+    check_direct16();
+    for (int T : {1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 300, 1000, 1024, 4096, 8192})
+        for (int causal = 0; causal < 2; ++causal) {
+            const int nq = (T + kBlockM - 1) / kBlockM;
+            for (int qt = 0; qt < nq; ++qt)
+                check_ring(key_tiles(qt, T, kBlockN16, causal), main_tiles(qt, T, kBlockN16, causal));
+        }
     // vt_pos16 is a permutation of one 64-key tile that keeps pairs adjacent
     std::set<int> pos;
     for (int key = 0; key < kBlockN16; ++key) pos.insert(vt_pos16(key));
@@ -249,6 +482,17 @@ int main() {
                 check16(BH, T, causal);
                 check32(BH, T, causal);
             }
+    for (int T : Ts)
+        for (int causal = 0; causal < 2; ++causal) {
+            check_pingpong(T, causal);
+            for (int BH : BHs) check_tile_map_bm(BH, T, causal);
+        }
+    for (int T : {8192, 32768, 131072})
+        for (int causal = 0; causal < 2; ++causal) {
+            check_pingpong(T, causal);
+            check_tile_map_bm(48, T, causal);
+            check_tile_map_bm(16, T, causal);
+        }
     // the large shapes: tile map and key cover only (enumeration is costly)
     const int bigT[] = {8192, 32768, 131072};
     for (int T : bigT)

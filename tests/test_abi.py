@@ -65,7 +65,7 @@ def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, T=8, D=64,
     (dict(scale=3e38), -1),  # |scale| * log2(e) overflows float
     (dict(q=FAKE + 8), -1), (dict(o=FAKE + 4), -1), (dict(lse=FAKE + 2), -1),
     (dict(B=65536, H=65536), -2),   # B*H beyond int32
-    (dict(B=4096, H=4096, T=128), -2),  # grid beyond one launch
+    (dict(B=4096, H=2048, T=256), -2),  # grid beyond one launch
 ])
 def test_fused_rejects_invalid(lib, kw, status):
     assert fwd(lib, **kw) == status

@@ -200,6 +200,23 @@ def test_late_spike(gpu_lib, dtype, T):
     check_full(gpu_lib, q, k, v, True, 0.125, dtype, f"late_spike_c_{dtype}_{T}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_rising_scores(gpu_lib, dtype, causal):
+    """Keys scaled up steadily along the sequence (x1 -> x6), so the running
+    maximum keeps growing tile after tile: the main-tile shortcut that
+    exponentiates against the previous maximum must hand over to the full
+    update whenever a weight could exceed its bound."""
+    T = 2048
+    q, k, v = make_qkv(1, 2, T, D, "f32", 1900)
+    ramp = torch.linspace(1.0, 6.0, T).reshape(1, 1, T, 1)
+    k = (k * ramp).to(dict(f32=torch.float32, bf16=torch.bfloat16,
+                           f16=torch.float16)[dtype])
+    q, v = (x.to(k.dtype) for x in (q, v))
+    check_full(gpu_lib, q, k, v, causal, 0.125, dtype,
+               f"rising_{dtype}_c{int(causal)}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
 def test_scale_sign_and_zero(gpu_lib, dtype, scale):
