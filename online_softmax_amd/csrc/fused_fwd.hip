@@ -216,62 +216,113 @@ __device__ inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until this wave's loads of a tile have landed, leaving `younger`
-// later tiles (4 load instructions each) in flight.
-__device__ inline void wait_tiles(int younger) {
-    if (younger >= 2)
-        wait_vmcnt<8>();
-    else if (younger == 1)
+// Wait until at most `in_flight` (0, 2, 4 or 6: whole load batches) of this
+// wave's loads are pending.
+__device__ inline void wait_loads(int in_flight) {
+    if (in_flight >= 6)
+        wait_vmcnt<6>();
+    else if (in_flight >= 4)
         wait_vmcnt<4>();
+    else if (in_flight >= 2)
+        wait_vmcnt<2>();
     else
         wait_vmcnt<0>();
 }
 
-// S^T = K Q^T for one 64-key tile from a swizzled LDS K tile.
-template <int DT>
-__device__ inline void qk16(const char* __restrict__ kb, const v4u32 (&qf)[4],
-                            v16f32 (&s)[2], int lane) {
-    const int ql = lane & 31, hh = lane >> 5;
-    v4u32 kf[2][4];
+// One direct load with a scalar base address: lane l fetches the 16 bytes at
+// sbase + voff (voff per lane) into LDS byte offset lds_off + 16 * l. No
+// per-lane address arithmetic is needed per tile.
+__device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+// A lane's LDS fragment addresses within a tile: one per K step (ko, the key
+// half-tile nt adds kKfragNtStride) and one per V half-tile (vo, the step ks
+// and half add kVtrKsStride and kVtrHalfStride).
+struct FragAddr {
+    uint32_t ko[4];
+    uint32_t vo[2];
+};
+
+// K fragments of one 64-key tile from a swizzled LDS K tile, and the product
+// S^T = K Q^T (two independent accumulation chains, interleaved).
+__device__ inline void kfrag16(const char* __restrict__ kb, v4u32 (&kf)[2][4],
+                               const FragAddr& fa) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            kf[nt][ks] = *(const v4u32*)(kb + kfrag_byte(ql, hh, nt, ks));
+            kf[nt][ks] = *(const v4u32*)(kb + fa.ko[ks] + kKfragNtStride * nt);
+}
+template <int DT>
+__device__ inline void qk16_mfma(const v4u32 (&kf)[2][4], const v4u32 (&qf)[4],
+                                 v16f32 (&s)[2]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s[nt] = mfma16<DT>(kf[nt][ks], qf[ks], s[nt]);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) s[nt] = mfma16<DT>(kf[nt][ks], qf[ks], s[nt]);
+}
+template <int DT>
+__device__ inline void qk16(const char* __restrict__ kb, const v4u32 (&qf)[4],
+                            v16f32 (&s)[2], const FragAddr& fa) {
+    v4u32 kf[2][4];
+    kfrag16(kb, kf, fa);
+    qk16_mfma<DT>(kf, qf, s);
 }
 
 // V^T fragments of one 64-key tile, by transposed LDS reads.
 __device__ inline void vfrag16(const char* __restrict__ vb, v4u32 (&vf)[2][4],
-                               int lane) {
+                               const FragAddr& fa) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+        // one address per half-tile; the compiler must not split it into
+        // per-read invariant sums, so the constant steps stay in the
+        // instructions' offset field
+        uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)vb + fa.vo[mt];
+        asm("" : "+v"(addr));
+        typedef __attribute__((address_space(3))) char lds_char;
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        lds_char* pm = (lds_char*)addr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(vb + vtr_byte(lane, mt, ks, 0)));
-            const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(vb + vtr_byte(lane, mt, ks, 1)));
+            lds_char* p = pm + kVtrKsStride * ks;
+            const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+            const v4i16 b =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + kVtrHalfStride));
             const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
             vf[mt][ks] = (v4u32){a2[0], a2[1], b2[0], b2[1]};
         }
+    }
 }
 
-// O^T += V^T P^T.
+// O^T += V^T P^T (two independent accumulation chains, interleaved).
 template <int DT>
 __device__ inline void pv16(const v4u32 (&vf)[2][4], const v4u32 (&pf)[4],
                             v16f32 (&oacc)[2]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int mt = 0; mt < 2; ++mt)
             oacc[mt] = mfma16<DT>(vf[mt][ks], pf[ks], oacc[mt]);
+}
+
+// Instruction order of one pipelined iteration: the LDS fragment reads
+// first, then each matrix product followed by an equal share of the vector
+// work, so the vector ALU issues while the matrix core runs.
+template <int NMFMA, int NVALU>
+__device__ inline void sched_iteration() {
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);  // VALU
+    }
 }
 
 // Row maximum of an unmasked S^T tile and the lazy reference update.
@@ -298,18 +349,19 @@ __device__ inline void lazy_update(const v16f32 (&s)[2], v16f32 (&oacc)[2],
 }
 
 // Weights of a main tile against the current reference (no mask, no max):
-// p = exp2(s*c - m*c) rounded into the P fragment, and their sum into l.
+// p = exp2(s*c - m*c) rounded into the P fragment; returns this lane's sum of
+// the rounded p.
 template <int DT>
-__device__ inline void weights16(const v16f32 (&s)[2], v4u32 (&pf)[4],
-                                 RowState& st, float c) {
+__device__ inline float weights16(const v16f32 (&s)[2], v4u32 (&pf)[4], float mc,
+                                  float c) {
     float t0 = 0.f, t1 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int nt = ks >> 1, r0 = (ks & 1) * 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float p0 = fast_exp2(fmaf(s[nt][r0 + 2 * i], c, -st.mc));
-            const float p1 = fast_exp2(fmaf(s[nt][r0 + 2 * i + 1], c, -st.mc));
+            const float p0 = fast_exp2(fmaf(s[nt][r0 + 2 * i], c, -mc));
+            const float p1 = fast_exp2(fmaf(s[nt][r0 + 2 * i + 1], c, -mc));
             pf[ks][i] = pack2<DT>(p0, p1);
             if (i & 1)
                 t1 = sum2<DT>(pf[ks][i], t1);
@@ -317,22 +369,45 @@ __device__ inline void weights16(const v16f32 (&s)[2], v4u32 (&pf)[4],
                 t0 = sum2<DT>(pf[ks][i], t0);
         }
     }
-    st.l += t0 + t1;
+    return t0 + t1;
 }
 
-// 4 waves, 32 query rows each. Main tiles (no mask) run software-pipelined:
-// iteration j computes S(j+1) = K(j+1) Q^T in the same block as the weights
-// of tile j and O += V(j) P(j), so a wave always has independent matrix and
-// vector work in flight; the (at most two) edge tiles run one at a time with
-// masks. K and V tiles arrive by direct global -> LDS loads three tiles ahead
-// into a 4-stage ring (schedule in fused_layout.h).
+// The lazy check of a main tile, taken after its weights: a lane's 32 weights
+// are each at most their sum t, so t <= 2^kLazyLog2 in every lane keeps every
+// weight within the bound without a row maximum (an overflow to inf fails the
+// test too). Otherwise (rare) S is recomputed from the K tile still in LDS,
+// the reference moves to the row maximum, O and l (which hold the earlier
+// tiles only) are rescaled and the weights recomputed.
+template <int DT>
+__device__ inline void lazy_check(const char* __restrict__ kb,
+                                  const v4u32 (&qf)[4], v4u32 (&pf)[4], float t,
+                                  v16f32 (&oacc)[2], RowState& st, float c,
+                                  const FragAddr& fa) {
+    if (__builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0) {
+        v16f32 s[2];
+        qk16<DT>(kb, qf, s, fa);
+        lazy_update(s, oacc, st, c);
+        t = weights16<DT>(s, pf, st.mc, c);
+    }
+    st.l += t;
+}
+
+// 4 waves, 32 query rows each. Main tiles (no mask) run as a three-stage
+// software pipeline: iteration j takes the weights of tile j (vector ALU)
+// while the matrix cores compute S(j+1) = K(j+1) Q^T and O += V(j-1) P(j-1),
+// none of which waits for this iteration's vector work; the lazy check of
+// tile j closes the iteration. The (at most two) edge tiles run one at a time
+// with masks. K and V tiles arrive by direct global -> LDS loads into rings
+// of their own, K three tiles ahead and V one (schedule in fused_layout.h);
+// K(j) stays resident through iteration j for the rare rescale.
 template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
     constexpr int BN = kBlockN16;
-    __shared__ __attribute__((aligned(1024))) char ring[kStages][2][kTileBytes16];
+    __shared__ __attribute__((aligned(1024))) char kring[kRingK][kTileBytes16];
+    __shared__ __attribute__((aligned(1024))) char vring[kRingV][kTileBytes16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -361,30 +436,47 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     }
     wait_vmcnt<0>();  // Q is in registers before the ring loads start
 
-    // Direct loads of tile t (K and V) into ring stage t % kStages: 4 wave
-    // instructions, 16 bytes per lane. Rows past T fetch row T-1 instead (a
-    // finite value whose weight the edge mask sets to 0).
+    // Direct loads (2 wave instructions, 16 bytes per lane, per K or V tile)
+    // from a scalar tile base and a fixed per-lane offset. The tile holding
+    // key T-1, when ragged, takes a per-lane path instead whose rows past T
+    // fetch row T-1 (a finite value whose weight the edge mask sets to 0).
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
-    int krow[2], kcol[2], vrow[2], vcol[2];
+    uint32_t kvoff[2], vvoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        dl_src(wave, i, lane, false, &krow[i], &kcol[i]);
-        dl_src(wave, i, lane, true, &vrow[i], &vcol[i]);
+        kvoff[i] = (uint32_t)dl_global_byte(wave, i, lane, false);
+        vvoff[i] = (uint32_t)dl_global_byte(wave, i, lane, true);
     }
-    auto issue = [&](int t) {
-        const int k0 = t * BN;
-        const uint32_t stage_off =
-            (uint32_t)(uintptr_t)(lds_void*)ring[t % kStages][0];
+    auto load_tile = [&](const uint16_t* src, uint32_t off, const uint32_t(&voff)[2],
+                         int tile) {
+        const int k0 = __builtin_amdgcn_readfirstlane(tile) * BN;  // uniform
+        if (k0 + BN <= T) {
+            const uint16_t* tb = src + (int64_t)k0 * kHeadDim;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rk = min(k0 + krow[i], T - 1);
-            const int rv = min(k0 + vrow[i], T - 1);
-            dma16(kh + (int64_t)rk * kHeadDim + 8 * kcol[i],
-                  stage_off + 1024 * (2 * wave_u + i));
-            dma16(vh + (int64_t)rv * kHeadDim + 8 * vcol[i],
-                  stage_off + kTileBytes16 + 1024 * (2 * wave_u + i));
+            for (int i = 0; i < 2; ++i)
+                dma16s(tb, voff[i], off + 1024 * (2 * wave_u + i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = (int)(voff[i] >> 7);
+                const int r = min(k0 + row, T - 1);
+                dma16(src + (int64_t)r * kHeadDim + ((voff[i] & 127) >> 1),
+                      off + 1024 * (2 * wave_u + i));
+            }
         }
     };
+    auto issue_batch = [&](int u) {
+        const int tk = batch_k(u, n_tiles), tv = batch_v(u, n_tiles);
+        if (tk >= 0)
+            load_tile(kh, (uint32_t)(uintptr_t)(lds_void*)kring[tk % kRingK], kvoff, tk);
+        if (tv >= 0)
+            load_tile(vh, (uint32_t)(uintptr_t)(lds_void*)vring[tv % kRingV], vvoff, tv);
+    };
+    FragAddr fa;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) fa.ko[ks] = (uint32_t)kfrag_byte(ql, hh, 0, ks);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) fa.vo[mt] = (uint32_t)vtr_byte(lane, mt, 0, 0);
 
     v16f32 oacc[2];
 #pragma unroll
@@ -394,53 +486,81 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     // reference max starts finite (-FLT_MAX): no inf - inf, and scale 0 works
     RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
 
-    for (int t = 0; t < 3 && t < n_tiles; ++t) issue(t);
+    for (int u = -3; u < 0; ++u) issue_batch(u);
 
-    // Main iteration j: S(j) is in scur with its reference update done.
+    // Main iteration j: S(j) is in scur (reference set for tile 0 by its row
+    // maximum), P(j-1) in pprev; produces P(j) in pcur and S(j+1) in snext.
     auto main_iter = [&](int j, v16f32(&scur)[2], v16f32(&snext)[2],
-                         auto next_tag) {
+                         v4u32(&pcur)[4], const v4u32(&pprev)[4], auto next_tag,
+                         auto prev_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
-        if (NEXT) wait_tiles(ring_younger(n_tiles, j, j + 1));
+        constexpr bool PREV = decltype(prev_tag)::value;
+        wait_loads(batch_size(j - 1, n_tiles));
         __syncthreads();
-        if (j + 3 < n_tiles) issue(j + 3);
-        v4u32 vf[2][4], pf[4];
-        vfrag16(ring[j % kStages][1], vf, lane);
-        weights16<DT>(scur, pf, st, c);
-        if (NEXT) qk16<DT>(ring[(j + 1) % kStages][0], qf, snext, lane);
-        pv16<DT>(vf, pf, oacc);
-        if (NEXT) lazy_update(snext, oacc, st, c);
+        issue_batch(j);
+        v4u32 vf[2][4], kf[2][4];
+        if (PREV) vfrag16(vring[(j + 2) % kRingV], vf, fa);  // V(j-1)
+        if (NEXT) kfrag16(kring[(j + 1) % kRingK], kf, fa);  // K(j+1)
+        __builtin_amdgcn_sched_barrier(0);  // the reads go first
+        const float t = weights16<DT>(scur, pcur, st.mc, c);
+        if (PREV) pv16<DT>(vf, pprev, oacc);
+        if (NEXT) qk16_mfma<DT>(kf, qf, snext);
+        constexpr int NM = 8 * NEXT + 8 * PREV;
+        if (NM > 0) sched_iteration<NM, 96 / (NM > 0 ? NM : 1)>();
+        lazy_check<DT>(kring[j % kRingK], qf, pcur, t, oacc, st, c, fa);
     };
 
+    bool synced = false;  // every issued load landed, all waves past a barrier
     if (n_main > 0) {
-        v16f32 sa[2], sb[2];
-        wait_tiles(ring_younger(n_tiles, 0, 0));
-        __syncthreads();
-        qk16<DT>(ring[0][0], qf, sa, lane);
-        lazy_update(sa, oacc, st, c);
         using Y = std::integral_constant<bool, true>;
         using N = std::integral_constant<bool, false>;
-        int j = 0;
-        for (; j + 2 < n_main; j += 2) {  // unrolled: S(j) ping-pongs sa/sb
-            main_iter(j, sa, sb, Y());
-            main_iter(j + 1, sb, sa, Y());
-        }
-        if (j + 1 < n_main) {
-            main_iter(j, sa, sb, Y());
-            main_iter(j + 1, sb, sa, N());
+        v16f32 sa[2], sb[2];
+        v4u32 pa[4], pb[4];
+        wait_loads(batch_size(-2, n_tiles) + batch_size(-1, n_tiles));
+        __syncthreads();
+        qk16<DT>(kring[0], qf, sa, fa);
+        lazy_update(sa, oacc, st, c);
+        // j = 0 has no product yet; then pairs so S and P ping-pong a/b
+        if (n_main == 1) {
+            main_iter(0, sa, sb, pa, pb, N(), N());
         } else {
-            main_iter(j, sa, sb, N());
+            main_iter(0, sa, sb, pa, pb, Y(), N());
+            int j = 1;
+            for (; j + 2 < n_main; j += 2) {
+                main_iter(j, sb, sa, pb, pa, Y(), Y());
+                main_iter(j + 1, sa, sb, pa, pb, Y(), Y());
+            }
+            if (j + 1 < n_main) {
+                main_iter(j, sb, sa, pb, pa, Y(), Y());
+                main_iter(j + 1, sa, sb, pa, pb, N(), Y());
+            } else {
+                main_iter(j, sb, sa, pb, pa, N(), Y());
+            }
         }
+        // the last main tile's product: its P is in pa when n_main is odd
+        wait_vmcnt<0>();
+        __syncthreads();
+        synced = true;
+        v4u32 vf[2][4];
+        vfrag16(vring[(n_main - 1) % kRingV], vf, fa);
+        if (n_main & 1)
+            pv16<DT>(vf, pa, oacc);
+        else
+            pv16<DT>(vf, pb, oacc);
     }
     // edge tiles (diagonal or ragged; at most two), one at a time
     for (int t = n_main; t < n_tiles; ++t) {
-        wait_tiles(ring_younger(n_tiles, t, t));
-        __syncthreads();
-        if (t + 3 < n_tiles) issue(t + 3);
+        if (!synced) {
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        synced = false;
+        issue_batch(t);
         if (!CAUSAL || t * BN <= wq0 + 31) {  // a wave skips tiles it cannot see
             v16f32 s[2];
             v4u32 vf[2][4], pf[4];
-            qk16<DT>(ring[t % kStages][0], qf, s, lane);
-            vfrag16(ring[t % kStages][1], vf, lane);
+            qk16<DT>(kring[t % kRingK], qf, s, fa);
+            vfrag16(vring[t % kRingV], vf, fa);
             softmax16<DT, CAUSAL, true>(s, pf, oacc, st, c, t * BN, T, my_q, hh);
             pv16<DT>(vf, pf, oacc);
         }

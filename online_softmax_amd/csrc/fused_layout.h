@@ -147,7 +147,6 @@ ATTN_HD int pp_v_tile_loaded(int p) { return p / 2; }       // p even
 //      16 consecutive rows at one chunk),
 //   V: chunk c of row r sits at slot c ^ ((r & 2) << 1)   (8-byte transposed
 //      reads of 4 consecutive rows x 4 chunks per 16 lanes).
-constexpr int kStages = 4;                 // LDS ring depth (tiles resident + in flight)
 constexpr int kTileBytes16 = kBlockN16 * kHeadDim * 2;   // 8 KiB per K or V tile
 ATTN_HD int swz_k(int row) { return (row >> 1) & 7; }
 ATTN_HD int swz_v(int row) { return (row & 2) << 1; }
@@ -164,20 +163,25 @@ ATTN_HD void dl_src(int w, int i, int l, bool is_v, int* row, int* chunk) {
     *row = slot >> 3;
     *chunk = (slot & 7) ^ (is_v ? swz_v(*row) : swz_k(*row));
 }
-// Ring schedule of the 16-bit kernel (n tiles; tile t lives in stage t % 4).
-// Tiles 0..2 are issued before the loop; iteration u (after its barrier)
-// issues tile u + 3. A main iteration j needs tile j+1 (for S(j+1)) and tile
-// j (V, waited for one iteration earlier); an edge iteration t needs tile t.
-// Before its barrier an iteration waits until the tile it needs has landed:
-// the younger tiles this wave may leave in flight number
-ATTN_HD int ring_younger(int n, int u, int needed) {
-    const int issued = (u + 2 < n - 1) ? u + 2 : n - 1;  // highest tile issued
-    return issued - needed;
+// Load schedule of the 16-bit kernel. K tiles and V tiles have rings of
+// their own: K tile t in stage t % 4, V tile t in stage t % 3. Batch u is
+// what the iteration u issues after its barrier: K(u + 3) and V(u + 1), each
+// when it exists (0 <= tile < n); the prologue issues batches -3, -2, -1,
+// i.e. K(0), K(1), then K(2) and V(0). Main iteration j (weights of tile j,
+// S(j+1) = K(j+1) Q^T, O += V(j-1) P(j-1), and in the rare rescale case S(j)
+// again from K(j)) reads K(j), K(j+1) and V(j-1), all in batch j - 2 or
+// older, so before its barrier a wave waits until only batch j - 1 is in
+// flight. The reloads of batch j go to K stage (j+3) % 4 (K(j-1), last read
+// in iteration j - 1) and V stage (j+1) % 3 (V(j-2), read in iteration j-1),
+// both finished by every wave at iteration j's barrier.
+ATTN_HD int batch_k(int u, int n) { return (u + 3 >= 0 && u + 3 < n) ? u + 3 : -1; }
+ATTN_HD int batch_v(int u, int n) { return (u + 1 >= 0 && u + 1 < n) ? u + 1 : -1; }
+// load instructions per wave in batch u (2 per K or V tile)
+ATTN_HD int batch_size(int u, int n) {
+    return 2 * (batch_k(u, n) >= 0) + 2 * (batch_v(u, n) >= 0);
 }
-// (4 load instructions per tile and wave). The stage that iteration u
-// reloads, (u + 3) % 4 = (u - 1) % 4, held tile u - 1, whose last reader is
-// iteration u - 1 (V of a main tile, or an edge tile), which every wave has
-// finished at iteration u's barrier.
+constexpr int kRingK = 4;
+constexpr int kRingV = 3;
 
 // K fragment of S^T tile nt, step ks for lane (ql, h): 16 bytes, dims
 // 16ks + 8h .. +7 of key 32nt + ql.
@@ -195,6 +199,22 @@ ATTN_HD int vtr_byte(int l, int mt, int ks, int half) {
     const int j = l & 15, r = j >> 2, c = j & 3;
     const int g = (l >> 4) & 1, h = l >> 5;
     return v_byte(16 * ks + 8 * half + 4 * h + r, 32 * mt + 16 * g + 4 * c);
+}
+// Both swizzles depend on the lane alone (bits 1..3 of the key row for K,
+// bit 1 for V), so a lane keeps one LDS address per K step ks and per V
+// half-tile mt and reaches the rest by constant offsets:
+//   kfrag_byte(ql, h, nt, ks)     = kfrag_byte(ql, h, 0, ks) + kKfragNtStride * nt
+//   vtr_byte(l, mt, ks, half)     = vtr_byte(l, mt, 0, 0) + kVtrKsStride * ks
+//                                   + kVtrHalfStride * half
+constexpr int kKfragNtStride = 32 * 128;
+constexpr int kVtrKsStride = 16 * 128;
+constexpr int kVtrHalfStride = 8 * 128;
+// Byte offset, within a K or V tile in global memory (64 rows of 128 B), of
+// the 16 bytes that direct load i of lane l of wave w fetches.
+ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
+    int row, chunk;
+    dl_src(w, i, l, is_v, &row, &chunk);
+    return row * kHeadDim * 2 + chunk * 16;
 }
 
 // ---- 16-bit staging: global -> registers -> LDS ---------------------------

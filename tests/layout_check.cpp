@@ -337,6 +337,8 @@ static void check_direct16() {
                     int row, chunk;
                     dl_src(w, i, l, is_v, &row, &chunk);
                     CHECK(row >= 0 && row < 64 && chunk >= 0 && chunk < 8, "dl_src range");
+                    CHECK(dl_global_byte(w, i, l, is_v) == row * 128 + chunk * 16,
+                          "direct load source offset");
                     const int dst = 1024 * (2 * w + i) + 16 * l;
                     const int want = is_v ? v_byte(row, 8 * chunk) : k_byte(row, chunk);
                     CHECK(dst == want, "direct load lands at the wrong slot");
@@ -351,6 +353,7 @@ static void check_direct16() {
                 const int ql = l & 31, h = l >> 5;
                 const int b = kfrag_byte(ql, h, nt, ks);
                 CHECK(b % 16 == 0 && b + 16 <= kTileBytes16, "kfrag range");
+                CHECK(b == kfrag_byte(ql, h, 0, ks) + kKfragNtStride * nt, "kfrag stride");
                 int row, dim;
                 decode_k(b, &row, &dim);
                 CHECK(row == 32 * nt + ql && dim == 16 * ks + 8 * h, "K fragment decode");
@@ -371,6 +374,9 @@ static void check_direct16() {
                 for (int l = 0; l < 64; ++l) {
                     addr[l] = vtr_byte(l, mt, ks, half);
                     CHECK(addr[l] % 8 == 0 && addr[l] + 8 <= kTileBytes16, "vtr range");
+                    CHECK(addr[l] == vtr_byte(l, mt, 0, 0) + kVtrKsStride * ks +
+                                         kVtrHalfStride * half,
+                          "vtr stride");
                 }
                 for (int l = 0; l < 64; ++l) {
                     const int g0 = l & ~15, i = l & 15;
@@ -397,63 +403,79 @@ static void check_direct16() {
             }
 }
 
-// The 4-stage ring: simulate per-wave issue order and vmcnt waits, check
-// each iteration reads tiles that have landed (given the wait) and that no
-// stage is reloaded while any wave may still read it.
+// The K / V rings of the 16-bit kernel: simulate one wave's issue order and
+// vmcnt waits (a wait leaving w loads in flight completes all older loads),
+// and check that each read finds its tile landed in its stage and that no
+// stage is reloaded after the barrier of an iteration that still reads it.
 static void check_ring(int n, int n_main) {
-    // loads issued per tile, in order; a wait "younger y" completes every
-    // tile except the y most recent ones issued
-    std::vector<int> stage_tile(kStages, -1);
-    std::vector<int> landed(n, 0);
-    int issued = -1;
-    auto issue = [&](int t) {
-        CHECK(t == issued + 1, "ring: tiles issued out of order");
-        issued = t;
-        stage_tile[t % kStages] = t;
+    std::vector<int> kst(kRingK, -1), vst(kRingV, -1);  // tile held per stage
+    std::vector<int> kdone(n, 0), vdone(n, 0);
+    std::vector<int> kread(n, -100), vread(n, -100);     // iteration of last read
+    struct Load { int tile; bool v; };
+    std::vector<Load> q;  // this wave's loads in issue order
+    int done = 0;         // loads completed (a prefix of q)
+    auto issue = [&](int u, int it) {
+        const int tk = batch_k(u, n), tv = batch_v(u, n);
+        if (tk >= 0) {
+            const int old = kst[tk % kRingK];
+            if (old >= 0) CHECK(kread[old] < it, "K stage of tile %d reloaded at %d", old, it);
+            kst[tk % kRingK] = tk;
+            q.push_back({tk, false}); q.push_back({tk, false});
+        }
+        if (tv >= 0) {
+            const int old = vst[tv % kRingV];
+            if (old >= 0) CHECK(vread[old] < it, "V stage of tile %d reloaded at %d", old, it);
+            vst[tv % kRingV] = tv;
+            q.push_back({tv, true}); q.push_back({tv, true});
+        }
     };
-    auto wait = [&](int younger) {
-        CHECK(younger >= 0 && younger <= 2, "ring: younger %d", younger);
-        for (int t = 0; t <= issued - younger; ++t) landed[t] = 1;
+    auto wait = [&](int in_flight) {
+        CHECK(in_flight >= 0 && in_flight <= (int)q.size(), "wait count");
+        done = (int)q.size() - in_flight;
+        for (int i = 0; i < done; ++i) (q[i].v ? vdone : kdone)[q[i].tile] = 1;
     };
-    for (int t = 0; t < 3 && t < n; ++t) issue(t);
-    // prologue S(0) (when tile 0 is a main tile)
+    auto needK = [&](int t, int it) {
+        CHECK(t >= 0 && t < n && kst[t % kRingK] == t && kdone[t], "K(%d) not ready at %d", t, it);
+        kread[t] = it;
+    };
+    auto needV = [&](int t, int it) {
+        CHECK(t >= 0 && t < n && vst[t % kRingV] == t && vdone[t], "V(%d) not ready at %d", t, it);
+        vread[t] = it;
+    };
+    for (int u = -3; u < 0; ++u) issue(u, -1);
     if (n_main > 0) {
-        wait(ring_younger(n, 0, 0));
-        CHECK(landed[0] && stage_tile[0] == 0, "ring: prologue tile 0");
+        wait(batch_size(-2, n) + batch_size(-1, n));  // K(0)
+        needK(0, -1);
+        for (int j = 0; j < n_main; ++j) {
+            wait(batch_size(j - 1, n));
+            issue(j, j);  // after the barrier
+            if (j + 1 < n_main) needK(j + 1, j);
+            if (j >= 1) needV(j - 1, j);
+            needK(j, j);  // the rescale case recomputes S(j)
+        }
     }
-    // last readers of each stage, as iteration indices
-    std::vector<int> k_read_at(n, -1), v_read_at(n, -1);
-    for (int u = 0; u < n; ++u) {
-        const bool main = u < n_main;
-        const int needed = main ? u + 1 : u;
-        if (main && u + 1 >= n_main) {
-            // last main iteration: no S(u+1); tile u was waited for before
-        } else {
-            wait(ring_younger(n, u, needed));
-            CHECK(needed < n && landed[needed], "ring: tile %d not landed at iteration %d", needed, u);
+    // barrier epochs: main iteration j is epoch j; the last product of the
+    // main tiles waits for everything, passes a barrier (epoch n_main) and
+    // leaves the first edge tile ready; each later edge tile waits and passes
+    // a barrier of its own
+    int epoch = n_main - 1;
+    bool synced = false;
+    if (n_main > 0) {
+        wait(0);
+        ++epoch;
+        synced = true;
+        needV(n_main - 1, epoch);
+    }
+    for (int t = n_main; t < n; ++t) {
+        if (!synced) {
+            wait(0);
+            ++epoch;
         }
-        // barrier: all waves finished iteration u - 1
-        if (u + 3 < n) {
-            const int old = stage_tile[(u + 3) % kStages];
-            if (old >= 0) {
-                CHECK(k_read_at[old] < u && v_read_at[old] < u,
-                      "ring: stage of tile %d reloaded at %d, read at %d/%d", old, u,
-                      k_read_at[old], v_read_at[old]);
-            }
-            issue(u + 3);
-        }
-        if (main) {
-            if (u + 1 < n_main) {
-                CHECK(stage_tile[(u + 1) % kStages] == u + 1 && landed[u + 1], "ring: K(%d)", u + 1);
-                k_read_at[u + 1] = u;
-            }
-            CHECK(stage_tile[u % kStages] == u && landed[u], "ring: V(%d)", u);
-            v_read_at[u] = u;
-            if (u == 0) k_read_at[0] = -1;
-        } else {
-            CHECK(stage_tile[u % kStages] == u && landed[u], "ring: edge tile %d", u);
-            k_read_at[u] = v_read_at[u] = u;
-        }
+        synced = false;
+        CHECK(batch_k(t, n) < 0, "edge iteration %d would load K", t);
+        issue(t, epoch);
+        needK(t, epoch);
+        needV(t, epoch);
     }
 }
 
