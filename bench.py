@@ -230,7 +230,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="a name from online_softmax_amd.inputs.WORKLOADS")
-    ap.add_argument("--cpu-rows", type=int, default=32768,
+    ap.add_argument("--cpu-rows", type=int, default=196608,
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contrast", action="store_true")

@@ -201,8 +201,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // wave-uniform). Issued as inline assembly so the compiler does not treat the
 // LDS write as aliasing every later LDS read and drain the load queue before
 // each tile; completion is tracked explicitly with wait_vmcnt and a barrier.
+// A load that takes its LDS address from M0 needs one wait state after the
+// scalar write of M0, hence the s_nop.
 __device__ inline void dma16(const void* gptr, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_off), "v"(gptr)
                  : "memory", "m0");
@@ -233,7 +235,7 @@ __device__ inline void wait_loads(int in_flight) {
 // sbase + voff (voff per lane) into LDS byte offset lds_off + 16 * l. No
 // per-lane address arithmetic is needed per tile.
 __device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_off), "v"(voff), "s"(sbase)
                  : "memory", "m0");
