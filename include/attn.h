@@ -61,7 +61,8 @@ typedef enum {
                                   workspace too small, a null output struct */
     ATTN_ERR_UNSUPPORTED = -2, /* a well-formed request this library does not
                                   implement: D != 64, a non-fp32 naive call,
-                                  or a grid larger than one launch holds     */
+                                  a grid larger than one launch holds, or a
+                                  16-bit slice over 4 GiB                    */
     ATTN_ERR_HIP = -3          /* the HIP runtime refused a launch or query;
                                   the code is kept for attn_last_hip_error() */
 } attn_status;
@@ -83,7 +84,10 @@ typedef enum { ATTN_PATH_FUSED = 0, ATTN_PATH_NAIVE = 1 } attn_path;
  * dtype   : an attn_dtype.
  * stream  : hipStream_t or NULL.
  *
- * Returns ATTN_OK once enqueued, or an error status with nothing enqueued.
+ * Returns ATTN_OK once enqueued, or an error status with nothing enqueued;
+ * ATTN_ERR_UNSUPPORTED also for a 16-bit dtype with T * D * 2 > 2^32 - 1
+ * bytes per (batch, head) slice (one K or V slice is addressed as a single
+ * buffer).
  * Extra device memory: none (the caller's lse is the only O(T) side output).
  */
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,

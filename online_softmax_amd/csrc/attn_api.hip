@@ -70,6 +70,10 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
     const uint64_t nq = ((uint64_t)T + bm - 1) / bm;
     if (nq * (uint64_t)B * (uint64_t)H > kMaxFusedWorkgroups)
         return ATTN_ERR_UNSUPPORTED;
+    // the 16-bit kernel addresses one (batch, head) slice of K or V through a
+    // buffer resource with a 32-bit byte size
+    if (dtype != ATTN_F32 && (uint64_t)T * D * 2 > UINT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
     // exp2 multiplier: |scale| * log2(e); a negative scale negates Q instead
     const double c = fabs((double)scale) * 1.4426950408889634073599;
     if (!isfinite((float)c)) return ATTN_ERR_INVALID;

@@ -196,17 +196,35 @@ __device__ inline void softmax16(v16f32 (&s)[2], v4u32 (&pf)[4],
 typedef short v4i16 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's bytes land at LDS byte offset lds_off + 16 * l (lds_off must be
-// wave-uniform). Issued as inline assembly so the compiler does not treat the
-// LDS write as aliasing every later LDS read and drain the load queue before
-// each tile; completion is tracked explicitly with wait_vmcnt and a barrier.
-// A load that takes its LDS address from M0 needs one wait state after the
-// scalar write of M0, hence the s_nop.
-__device__ inline void dma16(const void* gptr, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+typedef uint32_t v4u32_rsrc __attribute__((__vector_size__(16)));
+
+// Buffer resource over `bytes` bytes from `base` (raw, dword data format),
+// built from wave-uniform values so it lives in scalar registers.
+__device__ inline v4u32_rsrc buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    v4u32_rsrc r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One direct load of 16 bytes per lane from buffer `rsrc` into LDS
+// (buffer_load_dwordx4 ... lds): lane l fetches bytes soff + voff[l] of the
+// buffer and they land at LDS byte offset lds_off + 16 * l (lds_off and soff
+// wave-uniform). The buffer form is used because, measured on gfx950, its
+// issue is delayed far less than the flat/global form's while the other
+// wave on the SIMD runs matrix instructions. Issued as inline assembly so the
+// compiler does not treat the LDS write as aliasing every later LDS read and
+// drain the load queue before each tile; completion is tracked explicitly
+// with wait_vmcnt and a barrier. A load that takes its LDS address from M0
+// needs one wait state after the scalar write of M0, hence the s_nop.
+__device__ inline void dma16(v4u32_rsrc rsrc, uint32_t voff, uint32_t soff,
+                             uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(lds_off), "v"(gptr)
+                 : "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
 
@@ -229,16 +247,6 @@ __device__ inline void wait_loads(int in_flight) {
         wait_vmcnt<2>();
     else
         wait_vmcnt<0>();
-}
-
-// One direct load with a scalar base address: lane l fetches the 16 bytes at
-// sbase + voff (voff per lane) into LDS byte offset lds_off + 16 * l. No
-// per-lane address arithmetic is needed per tile.
-__device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_off), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
 }
 
 // A lane's LDS fragment addresses within a tile: one per K step (ko, the key
@@ -439,9 +447,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     wait_vmcnt<0>();  // Q is in registers before the ring loads start
 
     // Direct loads (2 wave instructions, 16 bytes per lane, per K or V tile)
-    // from a scalar tile base and a fixed per-lane offset. The tile holding
-    // key T-1, when ragged, takes a per-lane path instead whose rows past T
-    // fetch row T-1 (a finite value whose weight the edge mask sets to 0).
+    // from the slice's buffer: the lane's fixed offset within a tile plus the
+    // tile's offset as a scalar. The tile holding key T-1, when ragged, takes
+    // per-lane offsets instead whose rows past T fetch row T-1 (a finite value
+    // whose weight the edge mask sets to 0); the buffer's size (the slice)
+    // bounds every access in any case.
+    const uint32_t slice_bytes = (uint32_t)T * (kHeadDim * 2);
+    const v4u32_rsrc krs = buffer_rsrc(kh, slice_bytes);
+    const v4u32_rsrc vrs = buffer_rsrc(vh, slice_bytes);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
     uint32_t kvoff[2], vvoff[2];
 #pragma unroll
@@ -449,20 +462,19 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
         kvoff[i] = (uint32_t)dl_global_byte(wave, i, lane, false);
         vvoff[i] = (uint32_t)dl_global_byte(wave, i, lane, true);
     }
-    auto load_tile = [&](const uint16_t* src, uint32_t off, const uint32_t(&voff)[2],
+    auto load_tile = [&](v4u32_rsrc rs, uint32_t off, const uint32_t(&voff)[2],
                          int tile) {
         const int k0 = __builtin_amdgcn_readfirstlane(tile) * BN;  // uniform
         if (k0 + BN <= T) {
-            const uint16_t* tb = src + (int64_t)k0 * kHeadDim;
+            const uint32_t soff = (uint32_t)k0 * (kHeadDim * 2);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                dma16s(tb, voff[i], off + 1024 * (2 * wave_u + i));
+                dma16(rs, voff[i], soff, off + 1024 * (2 * wave_u + i));
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int row = (int)(voff[i] >> 7);
-                const int r = min(k0 + row, T - 1);
-                dma16(src + (int64_t)r * kHeadDim + ((voff[i] & 127) >> 1),
+                const int r = min(k0 + (int)(voff[i] >> 7), T - 1);
+                dma16(rs, (uint32_t)r * (kHeadDim * 2) + (voff[i] & 127), 0u,
                       off + 1024 * (2 * wave_u + i));
             }
         }
@@ -470,9 +482,9 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
     auto issue_batch = [&](int u) {
         const int tk = batch_k(u, n_tiles), tv = batch_v(u, n_tiles);
         if (tk >= 0)
-            load_tile(kh, (uint32_t)(uintptr_t)(lds_void*)kring[tk % kRingK], kvoff, tk);
+            load_tile(krs, (uint32_t)(uintptr_t)(lds_void*)kring[tk % kRingK], kvoff, tk);
         if (tv >= 0)
-            load_tile(vh, (uint32_t)(uintptr_t)(lds_void*)vring[tv % kRingV], vvoff, tv);
+            load_tile(vrs, (uint32_t)(uintptr_t)(lds_void*)vring[tv % kRingV], vvoff, tv);
     };
     FragAddr fa;
 #pragma unroll

@@ -26,8 +26,7 @@
 // slot s of lane-half h of its B operand for the same reduction index, so any
 // assignment of reduction indices to (half, slot) works as long as A and B
 // use the same one. The P fragment inherits its key order from the
-// accumulator layout; the transposed V tile in LDS stores its keys in the
-// matching order (vt_pos16) so a lane's 8 keys are 16 contiguous bytes.
+// accumulator layout; the fragments read from the K and V tiles follow it.
 #pragma once
 
 #include <stdint.h>
@@ -47,9 +46,6 @@ constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
 
 // ---- 16-bit (bf16 / f16) path -------------------------------------------
 constexpr int kBlockN16 = 64;     // keys per LDS tile
-constexpr int kLdsStride16 = 72;  // elements per LDS row: 64 + 8 pad (16 B)
-constexpr int kKTile16 = kBlockN16 * kLdsStride16;    // K tile, elements
-constexpr int kVTile16 = kHeadDim * kLdsStride16;     // V^T tile, elements
 
 // ---- fp32 path -----------------------------------------------------------
 constexpr int kBlockN32 = 32;
@@ -58,24 +54,14 @@ constexpr int kVStride32 = 36;    // floats per V^T row: 32 + 4 pad
 constexpr int kKTile32 = kBlockN32 * kKStride32;
 constexpr int kVTile32 = kHeadDim * kVStride32;
 
-static_assert(kLdsStride16 % 8 == 0, "16-bit LDS rows must stay 16-byte aligned");
 static_assert(kKStride32 % 4 == 0 && kVStride32 % 4 == 0,
               "fp32 LDS rows must stay 16-byte aligned");
-static_assert(2 * 2 * (kKTile16 + kVTile16) <= 64 * 1024,
-              "16-bit double-buffered K and V^T tiles must fit 64 KiB");
 static_assert(2 * 4 * (kKTile32 + kVTile32) <= 64 * 1024,
               "fp32 double-buffered K and V^T tiles must fit 64 KiB");
 
 // Row (key or head-dim index) held by accumulator register r of a lane in
 // lane-half h of a 32x32 MFMA output tile.
 ATTN_HD int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
-// Column of key `key` (0..63 within a tile) in the transposed V tile of the
-// 16-bit path: bits 2 and 3 of the key index are swapped, which puts the 8
-// keys a lane-half feeds one PV MFMA next to each other.
-ATTN_HD int vt_pos16(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 // Workgroup -> (slice bh, query tile qt). Workgroups are dealt round-robin
 // to the 8 XCDs, so when the count divides by 8 the consecutive logical tiles
@@ -117,25 +103,6 @@ ATTN_HD int main_tiles(int qt, int T, int bn, bool causal, int bm = kBlockM) {
     const int all = key_tiles(qt, T, bn, causal, bm);
     return n < all ? n : all;
 }
-
-// ---- 16-bit ping-pong schedule ----------------------------------------------
-// 8 waves, two groups of 4 (wave w is in group w / 4; SIMD s runs waves s and
-// s + 4). Each wave owns 32 query rows: 256 per workgroup. Tile j of a wave
-// is an MFMA phase (O += V(j-1) P(j-1), then S(j) = K(j) Q^T) followed by a
-// VALU phase (the softmax of S(j)); group g runs phase r = p - g of its own
-// sequence at workgroup phase p, so on every SIMD one wave's products overlap
-// the other wave's softmax. Phases end with a workgroup barrier.
-constexpr int kPPWaves = 8;
-constexpr int kPPThreads = 64 * kPPWaves;
-constexpr int kPPBlockM = 32 * kPPWaves;
-// Workgroup phases for n key tiles: group 1's last MFMA phase is 2n + 1.
-ATTN_HD int pp_phases(int n) { return 2 * n + 2; }
-// Staging of tile i: at the start of phase 2i, group 0 issues the global
-// loads of K(i+1) and group 1 those of V(i); at the end of phase 2i+1 they
-// are written to LDS, K(i+1) into K buffer (i+1)&1 and V(i) into V buffer
-// i&1. K(i) is read in phases 2i and 2i+1, V(i) in phases 2i+2 and 2i+3.
-ATTN_HD int pp_k_tile_loaded(int p) { return p / 2 + 1; }   // p even
-ATTN_HD int pp_v_tile_loaded(int p) { return p / 2; }       // p even
 
 // ---- 16-bit direct-to-LDS staging ---------------------------------------------
 // K and V tiles (64 keys x 64 dims, 128-byte rows, no padding) are written by
@@ -217,37 +184,8 @@ ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
     return row * kHeadDim * 2 + chunk * 16;
 }
 
-// ---- 16-bit staging: global -> registers -> LDS ---------------------------
-// K tile: 64 keys x 64 dims = 512 chunks of 16 B; thread t moves chunks
-// t and t + 256 (i = 0, 1): key row and first dim of chunk i.
-ATTN_HD void k_stage16(int t, int i, int* row, int* col) {
-    const int c = t + kThreads * i;
-    *row = c >> 3;
-    *col = (c & 7) * 8;
-}
-ATTN_HD int k_lds16(int row, int col) { return row * kLdsStride16 + col; }
-
-// V tile: thread t loads keys key0, key0 + 1 at dims dim0 .. dim0 + 7 and
-// writes them transposed (one 32-bit pair per dim). Lanes of a wave differ
-// in the key pair first so the 32-bit LDS writes fall on distinct banks.
-ATTN_HD void v_stage16(int t, int* key0, int* dim0) {
-    *key0 = 2 * (t & 31);
-    *dim0 = 8 * (t >> 5);
-}
-ATTN_HD int v_lds16(int dim, int key) {
-    return dim * kLdsStride16 + vt_pos16(key);
-}
-
 // Q fragment of lane-half h for reduction step ks: dims 16*ks + 8*h .. +7.
 ATTN_HD int q_col16(int h, int ks) { return 16 * ks + 8 * h; }
-// K fragment (A operand of S^T tile nt, step ks) read by lane (ql, h).
-ATTN_HD int kfrag16(int ql, int h, int nt, int ks) {
-    return (32 * nt + ql) * kLdsStride16 + 16 * ks + 8 * h;
-}
-// V^T fragment (A operand of O^T tile mt, step ks) read by lane (ql, h).
-ATTN_HD int vfrag16(int ql, int h, int mt, int ks) {
-    return (32 * mt + ql) * kLdsStride16 + 16 * ks + 8 * h;
-}
 
 // ---- fp32 staging ----------------------------------------------------------
 // K tile: 32 keys x 64 dims = 512 chunks of 16 B; chunks t and t + 256.

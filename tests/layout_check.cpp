@@ -42,25 +42,6 @@ static void check_tile_map(int BH, int T, bool causal) {
     for (int i = 0; i < total; ++i) CHECK(seen[i] == 1, "tile %d hit %d times", i, seen[i]);
 }
 
-static void check_tile_map_bm(int BH, int T, bool causal) {
-    const int nq = (T + kPPBlockM - 1) / kPPBlockM;
-    const int total = nq * BH;
-    std::vector<int> seen((size_t)total, 0);
-    for (int b = 0; b < total; ++b) {
-        int bh, qt;
-        tile_of(b, total, nq, causal, &bh, &qt);
-        CHECK(bh >= 0 && bh < BH && qt >= 0 && qt < nq, "tile_of(%d) out of range", b);
-        if (bh >= 0 && bh < BH && qt >= 0 && qt < nq) seen[(size_t)bh * nq + qt]++;
-        // every K/V row a workgroup loads is inside its slice
-        const int n = key_tiles(qt, T, kBlockN16, causal, kPPBlockM);
-        CHECK(n >= 1 && (long)(n - 1) * kBlockN16 < T, "bm256 key tiles");
-        int last = qt * kPPBlockM + kPPBlockM - 1;
-        if (last > T - 1) last = T - 1;
-        CHECK((long)n * kBlockN16 > (causal ? last : T - 1), "bm256 key cover");
-    }
-    for (int i = 0; i < total; ++i) CHECK(seen[i] == 1, "tile %d hit %d times", i, seen[i]);
-}
-
 static void check_key_cover(int T, int bn, bool causal) {
     const int nq = (T + kBlockM - 1) / kBlockM;
     for (int qt = 0; qt < nq; ++qt) {
@@ -93,71 +74,14 @@ static void check_key_cover(int T, int bn, bool causal) {
     }
 }
 
+// Global accesses of every 16-bit workgroup: the direct loads of every key
+// tile it reads (full tiles: the slice buffer at the tile's offset plus the
+// lane's offset; the ragged tile: rows clamped to T-1), its Q and O rows and
+// lse; and the Q and O dims of every lane.
 static void check16(int BH, int T, bool causal) {
-    const long tensor = (long)BH * T * kHeadDim;
+    const long tensor = (long)BH * T * kHeadDim;  // elements
+    const long slice_bytes = (long)T * kHeadDim * 2;
     const int nq = (T + kBlockM - 1) / kBlockM;
-    // LDS stage coverage (independent of the tile index)
-    std::vector<int> kcov(kKTile16, 0), vcov(kVTile16, 0);
-    for (int t = 0; t < kThreads; ++t) {
-        for (int i = 0; i < 2; ++i) {
-            int row, col;
-            k_stage16(t, i, &row, &col);
-            const int a = k_lds16(row, col);
-            CHECK(row >= 0 && row < kBlockN16 && col >= 0 && col + 8 <= kHeadDim, "k_stage16");
-            CHECK(a % 8 == 0 && a + 8 <= kKTile16, "k_lds16 %d", a);
-            for (int x = 0; x < 8; ++x) kcov[a + x]++;
-        }
-        int key0, dim0;
-        v_stage16(t, &key0, &dim0);
-        CHECK(key0 % 2 == 0 && key0 + 2 <= kBlockN16 && dim0 + 8 <= kHeadDim, "v_stage16");
-        for (int j = 0; j < 8; ++j) {
-            const int a = v_lds16(dim0 + j, key0);
-            CHECK(a % 2 == 0 && a + 2 <= kVTile16, "v_lds16 %d", a);
-            CHECK(v_lds16(dim0 + j, key0 + 1) == a + 1, "key pair not adjacent");
-            vcov[a]++;
-            vcov[a + 1]++;
-        }
-    }
-    for (int r = 0; r < kBlockN16; ++r)
-        for (int c = 0; c < kHeadDim; ++c)
-            CHECK(kcov[k_lds16(r, c)] == 1, "K lds (%d,%d) written %d times", r, c,
-                  kcov[k_lds16(r, c)]);
-    for (int d = 0; d < kHeadDim; ++d)
-        for (int key = 0; key < kBlockN16; ++key)
-            CHECK(vcov[v_lds16(d, key)] == 1, "V lds (%d,%d) written %d times", d, key,
-                  vcov[v_lds16(d, key)]);
-    // fragment reads, and the pairing of reduction indices
-    for (int lane = 0; lane < 64; ++lane) {
-        const int ql = lane & 31, hh = lane >> 5;
-        for (int ks = 0; ks < 4; ++ks) {
-            const int qc = q_col16(hh, ks);
-            CHECK(qc % 8 == 0 && qc + 8 <= kHeadDim, "q_col16");
-            for (int nt = 0; nt < 2; ++nt) {
-                const int a = kfrag16(ql, hh, nt, ks);
-                CHECK(a % 8 == 0 && a + 8 <= kKTile16, "kfrag16");
-                // A slot s of K = K[32nt + ql][qc + s]; B slot s of Q = dim qc + s
-                CHECK(a == k_lds16(32 * nt + ql, qc), "K/Q dim pairing");
-            }
-            for (int mt = 0; mt < 2; ++mt) {
-                const int a = vfrag16(ql, hh, mt, ks);
-                CHECK(a % 8 == 0 && a + 8 <= kVTile16, "vfrag16");
-                for (int s = 0; s < 8; ++s) {
-                    // key of P slot s of step ks (accumulator register r0 + s)
-                    const int nt = ks >> 1, r = (ks & 1) * 8 + s;
-                    const int pkey = 32 * nt + acc_row(r, hh);
-                    // key of V^T slot s at row 32mt + ql
-                    CHECK(a + s == v_lds16(32 * mt + ql, pkey),
-                          "P/V key mismatch lane %d ks %d slot %d", lane, ks, s);
-                }
-            }
-        }
-        for (int mt = 0; mt < 2; ++mt)
-            for (int g = 0; g < 4; ++g) {
-                const int d = 32 * mt + acc_row(4 * g, hh);
-                CHECK(d % 4 == 0 && d + 4 <= kHeadDim, "O store dims");
-            }
-    }
-    // global accesses of every workgroup
     const int total = nq * BH;
     for (int b = 0; b < total; ++b) {
         int bh, qt;
@@ -165,24 +89,25 @@ static void check16(int BH, int T, bool causal) {
         const long base = (long)bh * T * kHeadDim;
         const int n = key_tiles(qt, T, kBlockN16, causal);
         for (int kt = 0; kt < n; ++kt) {
-            const int k0 = kt * kBlockN16;
-            for (int t = 0; t < kThreads; ++t) {
-                for (int i = 0; i < 2; ++i) {
-                    int row, col;
-                    k_stage16(t, i, &row, &col);
-                    if (k0 + row < T) {
-                        const long a = base + (long)(k0 + row) * kHeadDim + col;
-                        CHECK(a >= 0 && a + 8 <= tensor && a % 8 == 0, "K global");
-                    }
-                }
-                int key0, dim0;
-                v_stage16(t, &key0, &dim0);
-                for (int e = 0; e < 2; ++e)
-                    if (k0 + key0 + e < T) {
-                        const long a = base + (long)(k0 + key0 + e) * kHeadDim + dim0;
-                        CHECK(a >= 0 && a + 8 <= tensor && a % 8 == 0, "V global");
-                    }
-            }
+            const long k0 = (long)kt * kBlockN16;
+            for (int w = 0; w < kWaves; ++w)
+                for (int i = 0; i < 2; ++i)
+                    for (int l = 0; l < 64; ++l)
+                        for (int is_v = 0; is_v < 2; ++is_v) {
+                            const long voff = dl_global_byte(w, i, l, is_v);
+                            long off;  // byte offset in the slice buffer
+                            if (k0 + kBlockN16 <= T) {
+                                off = k0 * kHeadDim * 2 + voff;
+                            } else {
+                                long r = k0 + (voff >> 7);
+                                if (r > T - 1) r = T - 1;
+                                off = r * kHeadDim * 2 + (voff & 127);
+                            }
+                            CHECK(off >= 0 && off + 16 <= slice_bytes && off % 16 == 0,
+                                  "direct load outside the slice: wg %d tile %d wave %d lane %d",
+                                  b, kt, w, l);
+                            CHECK(base + off / 2 + 8 <= tensor, "direct load outside the tensor");
+                        }
         }
         for (int t = 0; t < kThreads; ++t) {
             const int my_q = qt * kBlockM + 32 * (t >> 6) + (t & 31);
@@ -192,6 +117,18 @@ static void check16(int BH, int T, bool causal) {
                 CHECK((long)bh * T + my_q < (long)BH * T, "lse");
             }
         }
+    }
+    for (int lane = 0; lane < 64; ++lane) {
+        const int hh = lane >> 5;
+        for (int ks = 0; ks < 4; ++ks) {
+            const int qc = q_col16(hh, ks);
+            CHECK(qc % 8 == 0 && qc + 8 <= kHeadDim, "q_col16");
+        }
+        for (int mt = 0; mt < 2; ++mt)
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * mt + acc_row(4 * g, hh);
+                CHECK(d % 4 == 0 && d + 4 <= kHeadDim, "O store dims");
+            }
     }
 }
 
@@ -265,49 +202,6 @@ static void check32(int BH, int T, bool causal) {
                     }
             }
         }
-    }
-}
-
-// The 16-bit ping-pong schedule: simulate every phase of a launch and check
-// that each LDS read finds the tile it expects, written in an earlier phase,
-// and that no buffer is rewritten in a phase in which any wave still reads it
-// (a fast wave writes at the end of a phase while slow ones may still read).
-static void check_pingpong(int T, bool causal) {
-    const int nq = (T + kPPBlockM - 1) / kPPBlockM;
-    for (int qt = 0; qt < nq; ++qt) {
-        const int n = key_tiles(qt, T, kBlockN16, causal, kPPBlockM);
-        int kbuf[2] = {-1, -1}, vbuf[2] = {-1, -1};
-        kbuf[0] = 0;  // prologue
-        const int P = pp_phases(n);
-        for (int p = 0; p < P; ++p) {
-            bool kread[2] = {false, false}, vread[2] = {false, false};
-            for (int g = 0; g < 2; ++g) {
-                const int r = p - g;
-                if (r < 0 || (r & 1)) continue;  // only MFMA phases read LDS
-                const int i = r >> 1;
-                if (i >= 1 && i - 1 < n) {
-                    CHECK(vbuf[(i - 1) & 1] == i - 1, "qt %d p %d: V(%d) missing", qt, p, i - 1);
-                    vread[(i - 1) & 1] = true;
-                }
-                if (i < n) {
-                    CHECK(kbuf[i & 1] == i, "qt %d p %d: K(%d) missing (buf holds %d)", qt, p, i, kbuf[i & 1]);
-                    kread[i & 1] = true;
-                }
-            }
-            if (p & 1) {  // end of an odd phase: K(p/2 + 1), V(p/2) land
-                const int tk = pp_k_tile_loaded(p & ~1), tv = pp_v_tile_loaded(p & ~1);
-                if (tk < n) {
-                    CHECK(!kread[tk & 1], "qt %d p %d: K buffer %d rewritten while read", qt, p, tk & 1);
-                    kbuf[tk & 1] = tk;
-                }
-                if (tv < n) {
-                    CHECK(!vread[tv & 1], "qt %d p %d: V buffer %d rewritten while read", qt, p, tv & 1);
-                    vbuf[tv & 1] = tv;
-                }
-            }
-        }
-        // every tile's PV ran: the last MFMA phase of group 1 is P - 1
-        CHECK(((P - 1 - 1) >> 1) == n, "qt %d: schedule too short", qt);
     }
 }
 
@@ -487,11 +381,6 @@ int main() {
             for (int qt = 0; qt < nq; ++qt)
                 check_ring(key_tiles(qt, T, kBlockN16, causal), main_tiles(qt, T, kBlockN16, causal));
         }
-    // vt_pos16 is a permutation of one 64-key tile that keeps pairs adjacent
-    std::set<int> pos;
-    for (int key = 0; key < kBlockN16; ++key) pos.insert(vt_pos16(key));
-    CHECK((int)pos.size() == kBlockN16 && *pos.begin() == 0 &&
-              *pos.rbegin() == kBlockN16 - 1, "vt_pos16 not a permutation");
     const int Ts[] = {1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256,
                       257, 300, 1000, 1024, 4096};
     const int BHs[] = {1, 3, 6, 8, 48};
@@ -504,17 +393,6 @@ int main() {
                 check16(BH, T, causal);
                 check32(BH, T, causal);
             }
-    for (int T : Ts)
-        for (int causal = 0; causal < 2; ++causal) {
-            check_pingpong(T, causal);
-            for (int BH : BHs) check_tile_map_bm(BH, T, causal);
-        }
-    for (int T : {8192, 32768, 131072})
-        for (int causal = 0; causal < 2; ++causal) {
-            check_pingpong(T, causal);
-            check_tile_map_bm(48, T, causal);
-            check_tile_map_bm(16, T, causal);
-        }
     // the large shapes: tile map and key cover only (enumeration is costly)
     const int bigT[] = {8192, 32768, 131072};
     for (int T : bigT)
