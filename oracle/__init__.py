@@ -69,6 +69,11 @@ def _load():
             g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                           ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                           ctypes.c_void_p]
+            b = lib.oracle_attention_backward
+            b.restype = ctypes.c_int
+            b.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
+                ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                ctypes.c_int64] + [ctypes.c_void_p] * 3 + [ctypes.c_int]
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -144,3 +149,44 @@ def probabilities(q, k, causal: bool, scale: float) -> np.ndarray:
     if rc != 0:
         raise RuntimeError("oracle_probabilities failed (%d)" % rc)
     return P
+
+
+def attention_backward(q, k, v, dout, causal: bool, scale: float,
+                       slices=None, threads: int = 0):
+    """Exact gradients of attention in double precision.
+
+    q, k, v, dout: [B, H, T, D] (or [T, D] for one head), float32 or exactly
+    widenable to it; dout is the gradient of the loss with respect to the
+    output. slices: optional 1-D int array of slice ids b * H + h. Returns
+    (dq, dk, dv) as float64, each [B, H, T, D] (or [len(slices), T, D], or
+    [T, D] for one head), following "Flash attention in PyTorch, then in
+    Triton", section "Backwards, and training with it".
+    """
+    q, k, v, dout = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    single = q.ndim == 2
+    if single:
+        q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+    if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
+        raise ValueError("q, k, v, dout must share one [B, H, T, D] shape")
+    B, H, T, D = q.shape
+    if slices is not None:
+        slices = np.ascontiguousarray(np.asarray(slices, dtype=np.int64))
+        n = slices.shape[0]
+        shape = (n, T, D)
+        sptr = slices.ctypes.data
+    else:
+        n = B * H
+        shape = (B, H, T, D)
+        sptr = None
+    dq = np.empty(shape, np.float64)
+    dk = np.empty(shape, np.float64)
+    dv = np.empty(shape, np.float64)
+    rc = _load().oracle_attention_backward(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, B, H,
+        T, D, int(bool(causal)), float(scale), sptr, n, dq.ctypes.data,
+        dk.ctypes.data, dv.ctypes.data, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_backward failed (%d)" % rc)
+    if single and slices is None:
+        return dq[0, 0], dk[0, 0], dv[0, 0]
+    return dq, dk, dv

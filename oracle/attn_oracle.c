@@ -34,12 +34,27 @@
  * element the sums run over j (or e) in ascending order. Build without
  * fast-math and without floating-point contraction.
  *
+ * The backward pass (oracle_attention_backward), per (batch, head) slice,
+ * follows the steps of "Flash attention in PyTorch, then in Triton", section
+ * "Backwards, and training with it", in that order: for an output gradient
+ * dO, each row's lse and O are computed as above and delta_i = sum_e
+ * dO[i,e] * O[i,e]; then for every visible pair (i, j)
+ *   P_ij  = exp(s_ij - lse_i)          (the probabilities made again)
+ *   dP_ij = sum_e dO[i,e] * v[j,e]
+ *   dS_ij = P_ij * (dP_ij - delta_i)   (the softmax's backward)
+ * and dQ_i = scale * sum_j dS_ij k_j, dK_j = scale * sum_i dS_ij q_i,
+ * dV_j = sum_i P_ij dO_i, every sum ascending in its index.
+ *
  * Parity pins (each checked by the test suite against closed forms, library
  * routines or brute force, never against this file itself):
  *   T = 1 returns V; Q = 0 returns the (prefix) mean of V; one-hot scores
  *   select one V row; probability rows sum to 1; brute force on tiny shapes;
  *   float64 scaled_dot_product_attention on small shapes; key-shift,
  *   V-affine, causal-prefix, slice-independence and permutation invariants.
+ *   Backward: central differences of the forward; float64 autograd through
+ *   scaled_dot_product_attention; T = 1 and Q = 0 closed forms; the key
+ *   gradients sum to zero; dV does not depend on V; sum_i q_i.dQ_i equals
+ *   sum_j k_j.dK_j; causal rows do not see later rows.
  */
 #include <math.h>
 #include <stdint.h>
@@ -179,6 +194,140 @@ int oracle_probabilities(const float* q, const float* k, int64_t T, int64_t D,
         for (int64_t j = visible; j < T; ++j) row[j] = 0.0;
     }
     return 0;
+}
+
+/* s_ij = scale * q_i . k_j, P_ij = exp(s_ij - lse_i), dP_ij = dO_i . v_j and
+ * dS_ij = P_ij * (dP_ij - delta_i) for one visible pair of one slice (q, k,
+ * v, dout: float32 [T, D] of the slice). */
+static void oracle_pair(const float* q, const float* k, const float* v,
+                        const float* dout, int64_t D, double scale,
+                        const double* lse, const double* delta, int64_t i,
+                        int64_t j, double* P, double* dS) {
+    double dot = 0.0, dpv = 0.0;
+    for (int64_t e = 0; e < D; ++e) dot += (double)q[i * D + e] * (double)k[j * D + e];
+    for (int64_t e = 0; e < D; ++e) dpv += (double)dout[i * D + e] * (double)v[j * D + e];
+    *P = exp(scale * dot - lse[i]);
+    *dS = *P * (dpv - delta[i]);
+}
+
+/*
+ * Gradients of attention for whole (batch, head) slices.
+ *
+ * q, k, v, dout : float32, contiguous [B, H, T, D] (dout = dL/dO).
+ * slices        : slice ids b * H + h, or NULL for every slice in order.
+ * nslices       : number of entries of `slices` (ignored when NULL).
+ * dq, dk, dv    : double [nslices, T, D] (or [B*H, T, D] when slices is NULL).
+ * nthreads      : OpenMP threads (<= 0: the runtime default).
+ *
+ * Returns 0, -1 on invalid arguments (nothing written), -2 when scratch
+ * memory could not be allocated.
+ */
+int oracle_attention_backward(const float* q, const float* k, const float* v,
+                              const float* dout, int64_t B, int64_t H,
+                              int64_t T, int64_t D, int causal, double scale,
+                              const int64_t* slices, int64_t nslices,
+                              double* dq, double* dk, double* dv,
+                              int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 1 || H < 1 ||
+        T < 1 || D < 1)
+        return -1;
+    const int64_t n = slices ? nslices : B * H;
+    if (n < 0) return -1;
+    if (slices) {
+        for (int64_t r = 0; r < n; ++r) {
+            if (slices[r] < 0 || slices[r] >= B * H) return -1;
+        }
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#endif
+    double* lse = (double*)malloc((size_t)T * sizeof(double));
+    double* delta = (double*)malloc((size_t)T * sizeof(double));
+    if (!lse || !delta) {
+        free(lse);
+        free(delta);
+        return -2;
+    }
+    int bad = 0;
+    for (int64_t r = 0; r < n && !bad; ++r) {
+        const int64_t slice = slices ? slices[r] : r;
+        const float* qs = q + slice * T * D;
+        const float* ks = k + slice * T * D;
+        const float* vs = v + slice * T * D;
+        const float* ds = dout + slice * T * D;
+        double* dqs = dq + r * T * D;
+        double* dks = dk + r * T * D;
+        double* dvs = dv + r * T * D;
+
+        /* each row's lse and O, and delta_i = dO_i . O_i */
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nthreads)
+#endif
+        {
+            double* scratch = (double*)malloc((size_t)T * sizeof(double));
+            double* o_row = (double*)malloc((size_t)D * sizeof(double));
+            if (!scratch || !o_row) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+                bad = 1;
+            }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+            for (int64_t i = 0; i < T; ++i) {
+                if (!scratch || !o_row) continue;
+                oracle_one_row(qs + i * D, ks, vs, T, D, causal, scale, i,
+                               scratch, o_row, &lse[i]);
+                double d = 0.0;
+                for (int64_t e = 0; e < D; ++e) d += (double)ds[i * D + e] * o_row[e];
+                delta[i] = d;
+            }
+            free(scratch);
+            free(o_row);
+        }
+        if (bad) break;
+
+        /* dQ_i = scale * sum_j dS_ij k_j, j ascending */
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16)
+#endif
+        for (int64_t i = 0; i < T; ++i) {
+            const int64_t visible = causal ? (i + 1) : T;
+            double* g = dqs + i * D;
+            for (int64_t e = 0; e < D; ++e) g[e] = 0.0;
+            for (int64_t j = 0; j < visible; ++j) {
+                double P, dS;
+                oracle_pair(qs, ks, vs, ds, D, scale, lse, delta, i, j, &P, &dS);
+                for (int64_t e = 0; e < D; ++e) g[e] += dS * (double)ks[j * D + e];
+            }
+            for (int64_t e = 0; e < D; ++e) g[e] *= scale;
+        }
+
+        /* dK_j = scale * sum_i dS_ij q_i and dV_j = sum_i P_ij dO_i, i
+         * ascending over the queries that see key j */
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16)
+#endif
+        for (int64_t j = 0; j < T; ++j) {
+            double* gk = dks + j * D;
+            double* gv = dvs + j * D;
+            for (int64_t e = 0; e < D; ++e) gk[e] = gv[e] = 0.0;
+            for (int64_t i = causal ? j : 0; i < T; ++i) {
+                double P, dS;
+                oracle_pair(qs, ks, vs, ds, D, scale, lse, delta, i, j, &P, &dS);
+                for (int64_t e = 0; e < D; ++e) {
+                    gk[e] += dS * (double)qs[i * D + e];
+                    gv[e] += P * (double)ds[i * D + e];
+                }
+            }
+            for (int64_t e = 0; e < D; ++e) gk[e] *= scale;
+        }
+    }
+    free(lse);
+    free(delta);
+    (void)nthreads;
+    return bad ? -2 : 0;
 }
 
 /* Number of OpenMP threads a parallel region would use by default. */

@@ -1,7 +1,8 @@
 """The oracle's pins must catch plausible mistakes. Each case below plants one
 mistake in a copy of the oracle's C source (on the CPU, in a temporary
-directory), builds it, and runs the pin suite against that build: at least one
-pin must fail. The in-tree oracle is never modified."""
+directory), builds it, and runs the matching pin suite (forward or backward)
+against that build: at least one pin must fail. The in-tree oracle is never
+modified."""
 import os
 import subprocess
 import sys
@@ -39,8 +40,33 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(name, edits, tmp_path):
+# mistakes in the backward pass, checked against the backward's pins
+BACKWARD_MUTANTS = [
+    ("bwd_no_delta", [("*dS = *P * (dpv - delta[i]);", "*dS = *P * dpv;")]),
+    ("bwd_ds_sign", [("*dS = *P * (dpv - delta[i]);", "*dS = *P * (delta[i] - dpv);")]),
+    ("bwd_dq_scale_dropped", [("for (int64_t e = 0; e < D; ++e) g[e] *= scale;",
+                               "for (int64_t e = 0; e < D; ++e) g[e] *= 1.0;")]),
+    ("bwd_dk_scale_dropped", [("for (int64_t e = 0; e < D; ++e) gk[e] *= scale;",
+                               "for (int64_t e = 0; e < D; ++e) gk[e] *= 1.0;")]),
+    ("bwd_dv_from_ds", [("gv[e] += P * (double)ds[i * D + e];",
+                         "gv[e] += dS * (double)ds[i * D + e];")]),
+    ("bwd_dk_key_operand", [("gk[e] += dS * (double)qs[i * D + e];",
+                             "gk[e] += dS * (double)ks[i * D + e];")]),
+    ("bwd_dk_sees_masked_rows", [("for (int64_t i = causal ? j : 0; i < T; ++i) {",
+                                  "for (int64_t i = 0; i < T; ++i) {")]),
+    ("bwd_p_without_lse", [("*P = exp(scale * dot - lse[i]);", "*P = exp(scale * dot);")]),
+    ("bwd_dp_key_operand", [("dpv += (double)dout[i * D + e] * (double)v[j * D + e];",
+                             "dpv += (double)dout[i * D + e] * (double)k[j * D + e];")]),
+    ("bwd_delta_from_values", [("d += (double)ds[i * D + e] * o_row[e];",
+                                "d += (double)ds[i * D + e] * (double)vs[i * D + e];")]),
+]
+
+CASES = [(n, e, "test_oracle_pins.py") for n, e in MUTANTS] + \
+    [(n, e, "test_oracle_bwd_pins.py") for n, e in BACKWARD_MUTANTS]
+
+
+@pytest.mark.parametrize("name,edits,pins", CASES, ids=[c[0] for c in CASES])
+def test_pins_catch_mutant(name, edits, pins, tmp_path):
     src = open(oracle.SOURCE).read()
     for old, new in edits:
         assert old in src, f"mutation site {old!r} not found"
@@ -53,7 +79,7 @@ def test_pins_catch_mutant(name, edits, tmp_path):
     env = dict(os.environ, ATTN_ORACLE_LIBRARY=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q",
                         "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
