@@ -119,6 +119,48 @@ int attn_naive_fwd(const float* q, const float* k, const float* v, float* o,
 size_t attn_naive_workspace_bytes(int B, int H, int T);
 
 /*
+ * attn_bwd_stream - gradients of attention with respect to q, k and v (the
+ * backward pass of "Flash attention in PyTorch, then in Triton", section
+ * "Backwards, and training with it"): with P rebuilt from the scores and
+ * the forward's lse, delta = rowsum(dO * O), dS = P (dO V^T - delta),
+ *   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+ *
+ * q, k, v   : device, [B, H, T, D] of `dtype`, the forward's inputs.
+ * o, lse    : device, the forward's output ([B, H, T, D] of `dtype`) and
+ *             log-sum-exp (float32 [B, H, T], natural log), as attn_fwd
+ *             wrote them for the same causal and scale.
+ * dout      : device, [B, H, T, D] of `dtype`: dL/dO.
+ * dq, dk, dv: device, [B, H, T, D] of `dtype`, written (every element);
+ *             accumulated in float32, rounded to nearest even once.
+ * workspace : caller-owned device buffer of at least
+ *             attn_bwd_workspace_bytes(B, H, T) bytes (16-byte aligned); it
+ *             receives delta (float32 [B, H, T]); contents undefined after.
+ * B, H, T, D, causal, scale, stream: as in attn_fwd_stream.
+ * dtype     : ATTN_BF16 or ATTN_F16; ATTN_F32 returns ATTN_ERR_UNSUPPORTED.
+ *
+ * Returns ATTN_OK once enqueued, or an error status with nothing enqueued:
+ * ATTN_ERR_INVALID for a null pointer, a pointer not 16-byte aligned (lse: 4),
+ * a bad size or dtype, a non-finite scale or a short workspace;
+ * ATTN_ERR_UNSUPPORTED for D != 64, float32, or a grid or slice too large.
+ * Extra device memory: the caller's workspace only.
+ */
+int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int T,
+                    int D, int causal, float scale, int dtype, void* stream);
+
+/* Workspace bytes attn_bwd_stream needs: B*H*T*4 rounded up to 256 bytes; 0
+ * for sizes < 1 or when the count overflows 64 bits. */
+size_t attn_bwd_workspace_bytes(int B, int H, int T);
+
+/* Arithmetic convention for the backward pass: five products to the
+ * forward's two (dP, dV, dQ, dK and the recomputed scores), so 2.5 times
+ * attn_flops ("Flash attention in PyTorch, then in Triton", section
+ * "Backwards, and training with it"); the two-kernel split computes the
+ * scores and dP twice, which this count does not credit. */
+double attn_bwd_flops(int B, int H, int T, int D, int causal);
+
+/*
  * Memory traffic of one call, as arithmetic (no device is touched). The
  * page "attention.cu" prints these counts before any time is measured.
  *

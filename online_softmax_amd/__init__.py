@@ -1,6 +1,7 @@
-"""MI355X-native exact attention forward (head dim 64) on gfx950.
+"""MI355X-native exact attention (head dim 64) on gfx950: the fused
+online-softmax forward and its backward pass.
 
-The fused online-softmax kernels and the materialising contrast path live in
+The fused kernels, the backward kernels and the materialising contrast path live in
 libattn.so (csrc/, C ABI in include/attn.h); this package is its thin
 binding. Nothing here computes attention: every step runs in the HIP kernels,
 and without the built library every call raises.
@@ -8,7 +9,8 @@ and without the built library every call raises.
 from .binding import (  # noqa: F401
     ATTN_BF16, ATTN_ERR_HIP, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_F16,
     ATTN_F32, ATTN_OK, ATTN_PATH_FUSED, ATTN_PATH_NAIVE, EXPORTS, LIBRARY,
-    AttnError, attention, attn_flops, attn_fused_tile, attn_fwd,
+    AttnError, attention, attention_backward, attn_bwd_flops, attn_bwd_stream,
+    attn_bwd_workspace_bytes, attn_flops, attn_fused_tile, attn_fwd,
     attn_fwd_stream, attn_kernel_attributes, attn_kernel_count,
     attn_kernel_name, attn_last_hip_error, attn_naive_fwd,
     attn_naive_workspace_bytes, attn_status_string, attn_traffic_bytes,

@@ -23,9 +23,11 @@ ATTN_PATH_FUSED, ATTN_PATH_NAIVE = 0, 1
 
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
-           "attn_naive_workspace_bytes", "attn_traffic_bytes", "attn_flops",
-           "attn_status_string", "attn_last_hip_error", "attn_kernel_count",
-           "attn_kernel_name", "attn_kernel_attributes", "attn_fused_tile")
+           "attn_naive_workspace_bytes", "attn_bwd_stream",
+           "attn_bwd_workspace_bytes", "attn_bwd_flops", "attn_traffic_bytes",
+           "attn_flops", "attn_status_string", "attn_last_hip_error",
+           "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
+           "attn_fused_tile")
 
 
 class AttnError(RuntimeError):
@@ -72,6 +74,11 @@ def load(path: str = LIBRARY):
                                        I, P]
         lib.attn_naive_workspace_bytes.argtypes = [I, I, I]
         lib.attn_naive_workspace_bytes.restype = S
+        lib.attn_bwd_stream.argtypes = [P] * 10 + [S, I, I, I, I, I, F, I, P]
+        lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
+        lib.attn_bwd_workspace_bytes.restype = S
+        lib.attn_bwd_flops.argtypes = [I, I, I, I, I]
+        lib.attn_bwd_flops.restype = ctypes.c_double
         lib.attn_traffic_bytes.argtypes = [I, I, I, I, I, I, I,
                                            ctypes.POINTER(attn_traffic)]
         lib.attn_flops.argtypes = [I, I, I, I, I]
@@ -163,6 +170,29 @@ def attn_naive_fwd(q, k, v, o, lse, workspace, causal: bool, scale: float,
     _check(st, "attn_naive_fwd")
 
 
+def attn_bwd_workspace_bytes(B: int, H: int, T: int) -> int:
+    return int(_lib().attn_bwd_workspace_bytes(B, H, T))
+
+
+def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
+                    scale: float, stream=None):
+    """Backward pass into caller-owned dq, dk, dv (q's shape and dtype);
+    workspace is a device tensor of at least attn_bwd_workspace_bytes(B, H,
+    T) bytes."""
+    B, H, T, D = _dims(q)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib().attn_bwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(workspace), nbytes, B, H, T, D,
+                                int(bool(causal)), float(scale), dtype_code(q),
+                                _stream(stream, q.device))
+    _check(st, "attn_bwd_stream")
+
+
+def attn_bwd_flops(B: int, H: int, T: int, D: int, causal: bool) -> float:
+    return float(_lib().attn_bwd_flops(B, H, T, D, int(bool(causal))))
+
+
 def attn_traffic_bytes(path: int, B: int, H: int, T: int, D: int, dtype: int,
                        causal: bool) -> dict:
     out = attn_traffic()
@@ -220,3 +250,19 @@ def attention(q, k, v, causal: bool = True, scale: float | None = None,
         if with_lse else None
     attn_fwd_stream(q, k, v, o, lse, causal, scale, stream)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = True,
+                       scale: float | None = None, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch on q's device and run
+    the backward pass for the forward (o, lse) of the same q, k, v, causal and
+    scale. Returns (dq, dk, dv)."""
+    import torch
+    B, H, T, D = _dims(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(attn_bwd_workspace_bytes(B, H, T), dtype=torch.uint8,
+                     device=q.device)
+    attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
+    return dq, dk, dv

@@ -90,6 +90,55 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            nullptr);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int T) {
+    if (B < 1 || H < 1 || T < 1) return 0;
+    uint64_t bh, rows, bytes;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh)) return 0;
+    if (!mul_ok(bh, (uint64_t)T, &rows)) return 0;
+    if (!mul_ok(rows, 4, &bytes)) return 0;
+    if (bytes > UINT64_MAX - 255) return 0;
+    return (size_t)((bytes + 255) & ~(uint64_t)255);
+}
+
+int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, int B, int H, int T,
+                    int D, int causal, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    const void* p16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* p : p16)
+        if (!aligned16(p)) return ATTN_ERR_INVALID;
+    if (!aligned4(lse)) return ATTN_ERR_INVALID;
+    const size_t need = attn_bwd_workspace_bytes(B, H, T);
+    if (need == 0) return ATTN_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return ATTN_ERR_INVALID;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t nkb = ((uint64_t)T + attn::kBwdBlockKV - 1) / attn::kBwdBlockKV;
+    const uint64_t nq = ((uint64_t)T + attn::kBlockM - 1) / attn::kBlockM;
+    if (nkb * bh > kMaxFusedWorkgroups || nq * bh > kMaxFusedWorkgroups ||
+        (bh * T + 31) / 32 > (uint64_t)INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
+    if ((uint64_t)T * D * 2 > UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const double c = fabs((double)scale) * 1.4426950408889634073599;
+    if (!isfinite((float)c)) return ATTN_ERR_INVALID;
+    const hipError_t e = attn::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv,
+                                          (float*)workspace, B * H, T, causal ? 1 : 0,
+                                          (float)c, scale, scale < 0.0f, dtype,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
+double attn_bwd_flops(int B, int H, int T, int D, int causal) {
+    return 2.5 * attn_flops(B, H, T, D, causal);
+}
+
 size_t attn_naive_workspace_bytes(int B, int H, int T) {
     if (B < 1 || H < 1 || T < 1) return 0;
     uint64_t bh, tt, table, two, rows, total;
@@ -204,7 +253,9 @@ const char* attn_status_string(int status) {
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
 
-int attn_kernel_count(void) { return attn::kFusedKernels + attn::kNaiveKernels; }
+int attn_kernel_count(void) {
+    return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels;
+}
 
 const char* attn_kernel_name(int kernel) {
     static const char* const names[] = {
@@ -212,7 +263,12 @@ const char* attn_kernel_name(int kernel) {
         "fused_fwd16<f16, causal>",  "fused_fwd16<f16, full>",
         "fused_fwd32<causal>",       "fused_fwd32<full>",
         "naive_scores",              "naive_softmax",
-        "naive_weighted_v"};
+        "naive_weighted_v",
+        "bwd_delta16<bf16>",         "bwd_kv16<bf16, causal>",
+        "bwd_kv16<bf16, full>",      "bwd_q16<bf16, causal>",
+        "bwd_q16<bf16, full>",       "bwd_delta16<f16>",
+        "bwd_kv16<f16, causal>",     "bwd_kv16<f16, full>",
+        "bwd_q16<f16, causal>",      "bwd_q16<f16, full>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -220,9 +276,10 @@ const char* attn_kernel_name(int kernel) {
 int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     if (!out || kernel < 0 || kernel >= attn_kernel_count())
         return ATTN_ERR_INVALID;
-    const void* fn = kernel < attn::kFusedKernels
-                         ? attn::fused_kernel_ptr(kernel)
-                         : attn::naive_kernel_ptr(kernel - attn::kFusedKernels);
+    const int naive0 = attn::kFusedKernels, bwd0 = naive0 + attn::kNaiveKernels;
+    const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
+                     : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
+                                     : attn::bwd_kernel_ptr(kernel - bwd0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);

@@ -184,6 +184,71 @@ ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
     return row * kHeadDim * 2 + chunk * 16;
 }
 
+// ---- backward pass (16-bit) -----------------------------------------------
+// The backward kernels read some 64-row tiles both ways: row fragments
+// (16 consecutive rows at one 16-byte chunk per quarter-wave, as the K tile
+// of the forward) and transposed fragments (4 rows x 4 columns per 16 lanes,
+// as the V tile of the forward). One swizzle serves both without bank
+// conflicts: chunk c of row r sits at slot c ^ swz_b(r), where
+//   swz_b(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+// is a bijection of bits 1..3 of the row (16 consecutive rows of one parity
+// land on 8 distinct slots) and flips slot bit 2 between rows r and r + 2 of
+// a group of four (the two halves of a transposed read's row quad land on
+// disjoint slots).
+constexpr int kBwdBlockKV = 128;  // keys per workgroup of the dK/dV kernel
+constexpr int kBwdBlockQ = 64;    // queries per tile it streams
+ATTN_HD int swz_b(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+ATTN_HD int b_byte(int row, int chunk) { return row * 128 + ((chunk ^ swz_b(row)) << 4); }
+ATTN_HD int b_elem_byte(int row, int d) {
+    return row * 128 + (((d >> 3) ^ swz_b(row)) << 4) + ((d & 7) << 1);
+}
+// Direct load of a backward tile: wave w's instruction i (0, 1), lane l ->
+// tile row and logical chunk (it lands at byte 1024*(2w+i) + 16*l).
+ATTN_HD void dlb_src(int w, int i, int l, int* row, int* chunk) {
+    const int slot = (2 * w + i) * 64 + l;
+    *row = slot >> 3;
+    *chunk = (slot & 7) ^ swz_b(*row);
+}
+ATTN_HD int dlb_global_byte(int w, int i, int l) {
+    int row, chunk;
+    dlb_src(w, i, l, &row, &chunk);
+    return row * kHeadDim * 2 + chunk * 16;
+}
+// Row fragment (A operand: 32 rows of tile half mt, reduction step ks over
+// the 64 columns) of lane (ql, h): 16 bytes, columns 16ks + 8h .. +7 of row
+// 32mt + ql. The row half mt adds 4096 bytes; the step needs a lane base.
+ATTN_HD int bfrag_byte(int ql, int h, int mt, int ks) {
+    return b_byte(32 * mt + ql, 2 * ks + h);
+}
+// Transposed fragment (A operand: columns 32ct .. +31 as rows, reduction over
+// 16 tile rows per step ks) read by lane l as two 8-byte transposing reads
+// (half 0, 1): the same lane pattern as the forward's V tile, in swz_b. The
+// step ks adds 2048 bytes; (ct, half) need a lane base each.
+ATTN_HD int btr_byte(int l, int ct, int ks, int half) {
+    const int j = l & 15, r = j >> 2, c = j & 3;
+    const int g = (l >> 4) & 1, h = l >> 5;
+    return b_elem_byte(16 * ks + 8 * half + 4 * h + r, 32 * ct + 16 * g + 4 * c);
+}
+constexpr int kBfragMtStride = 32 * 128;
+constexpr int kBtrKsStride = 16 * 128;
+// Workgroup -> (slice bh, key block kb) of the dK/dV kernel: XCD-grouped like
+// tile_of; causal launches take the heaviest (first) key blocks first, as
+// key block kb is seen by the queries from kb * kBwdBlockKV on.
+ATTN_HD void bwd_kv_tile_of(int block, int total, int nkb, bool causal, int* bh, int* kb) {
+    int L = block;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        L = (block & 7) * per + (block >> 3);
+    }
+    *bh = L / nkb;
+    const int t = L - *bh * nkb;
+    *kb = causal ? t : nkb - 1 - t;
+}
+// First query tile (of kBwdBlockQ) that sees any key of key block kb.
+ATTN_HD int bwd_first_qtile(int kb, bool causal) {
+    return causal ? (kb * kBwdBlockKV) / kBwdBlockQ : 0;
+}
+
 // Q fragment of lane-half h for reduction step ks: dims 16*ks + 8*h .. +7.
 ATTN_HD int q_col16(int h, int ks) { return 16 * ks + 8 * h; }
 

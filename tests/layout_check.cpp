@@ -297,6 +297,150 @@ static void check_direct16() {
             }
 }
 
+// The backward tiles in swz_b: direct-load coverage, row fragments (decode,
+// strides, bank conflicts), and transposed fragments simulated with the
+// hardware rule, which must hand lane (column, half h) slot s of step ks the
+// row the P / dS fragments hold there: 16ks + 8(s/4) + 4h + s%4.
+static void decode_b(int byte, int* row, int* dim) {
+    *row = byte / 128;
+    const int slot = (byte % 128) / 16;
+    *dim = ((slot ^ swz_b(*row)) * 8) + (byte % 16) / 2;
+}
+static void check_bwd_layout() {
+    std::vector<int> cov(64 * 8, 0);
+    for (int w = 0; w < kWaves; ++w)
+        for (int i = 0; i < 2; ++i)
+            for (int l = 0; l < 64; ++l) {
+                int row, chunk;
+                dlb_src(w, i, l, &row, &chunk);
+                CHECK(row >= 0 && row < 64 && chunk >= 0 && chunk < 8, "dlb_src range");
+                CHECK(1024 * (2 * w + i) + 16 * l == b_byte(row, chunk), "bwd direct load slot");
+                CHECK(dlb_global_byte(w, i, l) == row * 128 + chunk * 16, "bwd load offset");
+                cov[row * 8 + chunk]++;
+            }
+    for (int x = 0; x < 64 * 8; ++x) CHECK(cov[x] == 1, "bwd tile chunk fetched %d times", cov[x]);
+    for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < 4; ++ks) {
+            for (int l = 0; l < 64; ++l) {
+                const int ql = l & 31, h = l >> 5;
+                const int b = bfrag_byte(ql, h, mt, ks);
+                CHECK(b % 16 == 0 && b + 16 <= kTileBytes16, "bfrag range");
+                CHECK(b == bfrag_byte(ql, h, 0, ks) + kBfragMtStride * mt, "bfrag stride");
+                int row, dim;
+                decode_b(b, &row, &dim);
+                CHECK(row == 32 * mt + ql && dim == 16 * ks + 8 * h, "bwd row fragment decode");
+            }
+            for (int grp = 0; grp < 4; ++grp) {
+                std::vector<int> used(64, 0);
+                for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+                    const int b = bfrag_byte(l & 31, l >> 5, mt, ks);
+                    for (int x = 0; x < 4; ++x) used[(b / 4 + x) % 64]++;
+                }
+                for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "bwd row read bank conflict");
+            }
+        }
+    for (int ct = 0; ct < 2; ++ct)
+        for (int ks = 0; ks < 4; ++ks)
+            for (int half = 0; half < 2; ++half) {
+                int addr[64];
+                for (int l = 0; l < 64; ++l) {
+                    addr[l] = btr_byte(l, ct, ks, half);
+                    CHECK(addr[l] % 8 == 0 && addr[l] + 8 <= kTileBytes16, "btr range");
+                    CHECK(addr[l] == btr_byte(l, ct, 0, half) + kBtrKsStride * ks, "btr stride");
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int g0 = l & ~15, i = l & 15, h = l >> 5;
+                    for (int r = 0; r < 4; ++r) {
+                        const int src = g0 + 4 * r + i / 4;
+                        int row, dim;
+                        decode_b(addr[src] + 2 * (i % 4), &row, &dim);
+                        const int s = 4 * half + r;
+                        const int want_row = 16 * ks + 8 * (s / 4) + 4 * h + s % 4;
+                        // the P / dS packing of step ks holds accumulator
+                        // register 8(ks&1) + s of half-tile ks>>1
+                        const int pk = 32 * (ks >> 1) + acc_row(8 * (ks & 1) + s, h);
+                        CHECK(want_row == pk, "bwd packing order");
+                        CHECK(row == want_row && dim == 32 * ct + (l & 31),
+                              "bwd tr lane %d slot %d: row %d dim %d", l, s, row, dim);
+                    }
+                }
+                for (int half32 = 0; half32 < 2; ++half32) {
+                    std::vector<int> used(64, 0);
+                    for (int l = 32 * half32; l < 32 * half32 + 32; ++l)
+                        for (int x = 0; x < 2; ++x) used[(addr[l] / 4 + x) % 64]++;
+                    for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "bwd tr read bank conflict");
+                }
+            }
+}
+
+// The dK/dV kernel's work map: every (slice, key block) exactly once, and the
+// first query tile it streams holds the first query that sees its first key.
+static void check_bwd_map(int BH, int T, bool causal) {
+    const int nkb = (T + kBwdBlockKV - 1) / kBwdBlockKV;
+    const int nqt = (T + kBwdBlockQ - 1) / kBwdBlockQ;
+    const int total = nkb * BH;
+    std::vector<int> seen((size_t)total, 0);
+    for (int b = 0; b < total; ++b) {
+        int bh, kb;
+        bwd_kv_tile_of(b, total, nkb, causal, &bh, &kb);
+        CHECK(bh >= 0 && bh < BH && kb >= 0 && kb < nkb, "bwd_kv_tile_of range");
+        if (bh >= 0 && bh < BH && kb >= 0 && kb < nkb) seen[(size_t)bh * nkb + kb]++;
+        const int t0 = bwd_first_qtile(kb, causal);
+        CHECK(t0 >= 0 && t0 < nqt, "first query tile %d of %d", t0, nqt);
+        if (causal) {
+            CHECK((long)t0 * kBwdBlockQ <= (long)kb * kBwdBlockKV, "first tile starts late");
+            CHECK((long)(t0 + 1) * kBwdBlockQ > (long)kb * kBwdBlockKV, "first tile sees nothing");
+        }
+    }
+    for (int i = 0; i < total; ++i) CHECK(seen[i] == 1, "key block %d hit %d times", i, seen[i]);
+}
+
+// Global accesses of the backward kernels: the tile loads of every
+// workgroup (rows clamped to T-1 in a ragged tile), the lse/delta loads,
+// and the rows each lane reads into registers and writes.
+static void check_bwd_access(int BH, int T, bool causal) {
+    const long slice_bytes = (long)T * kHeadDim * 2;
+    auto tile_ok = [&](long row0, const char* what) {
+        for (int w = 0; w < kWaves; ++w)
+            for (int i = 0; i < 2; ++i)
+                for (int l = 0; l < 64; ++l) {
+                    const long voff = dlb_global_byte(w, i, l);
+                    long off;
+                    if (row0 + 64 <= T) {
+                        off = row0 * 128 + voff;
+                    } else {
+                        long r = row0 + (voff >> 7);
+                        if (r > T - 1) r = T - 1;
+                        off = r * 128 + (voff & 127);
+                    }
+                    CHECK(off >= 0 && off + 16 <= slice_bytes, "%s tile load outside slice", what);
+                }
+    };
+    const int nkb = (T + kBwdBlockKV - 1) / kBwdBlockKV;
+    const int nqt = (T + kBwdBlockQ - 1) / kBwdBlockQ;
+    for (int b = 0; b < nkb * BH; ++b) {
+        int bh, kb;
+        bwd_kv_tile_of(b, nkb * BH, nkb, causal, &bh, &kb);
+        CHECK(bh >= 0 && bh < BH, "bwd slice");
+        for (int u = bwd_first_qtile(kb, causal); u < nqt; ++u) {
+            const long q0 = (long)u * kBwdBlockQ;
+            tile_ok(q0, "bwd_kv");
+            for (int l = 0; l < 64; ++l) {
+                long r = q0 + l;
+                if (r > T - 1) r = T - 1;
+                CHECK(r >= 0 && r * 4 + 4 <= (long)T * 4, "lse/delta load");
+            }
+        }
+    }
+    const int nq = (T + kBlockM - 1) / kBlockM;
+    for (int b = 0; b < nq * BH; ++b) {
+        int bh, qt;
+        tile_of(b, nq * BH, nq, causal, &bh, &qt);
+        const int n = key_tiles(qt, T, kBlockN16, causal);
+        for (int u = 0; u < n; ++u) tile_ok((long)u * kBlockN16, "bwd_q");
+    }
+}
+
 // The K / V rings of the 16-bit kernel: simulate one wave's issue order and
 // vmcnt waits (a wait leaving w loads in flight completes all older loads),
 // and check that each read finds its tile landed in its stage and that no
@@ -375,6 +519,13 @@ static void check_ring(int n, int n_main) {
 
 int main() {
     check_direct16();
+    check_bwd_layout();
+    for (int T : {1, 63, 64, 65, 127, 128, 129, 300, 1000, 8192})
+        for (int BH : {1, 6, 48})
+            for (int causal = 0; causal < 2; ++causal) {
+                check_bwd_map(BH, T, causal);
+                check_bwd_access(BH, T, causal);
+            }
     for (int T : {1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 300, 1000, 1024, 4096, 8192})
         for (int causal = 0; causal < 2; ++causal) {
             const int nq = (T + kBlockM - 1) / kBlockM;

@@ -93,6 +93,36 @@ def test_naive_rejects_invalid(lib, kw, status):
     assert naive(lib, **kw) == status
 
 
+def bwd(lib, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1,
+        H=1, T=8, D=64, dtype=1, scale=0.125):
+    return lib.attn_bwd_stream(q, FAKE, FAKE, o, FAKE, lse, dq, FAKE, FAKE, ws,
+                               ws_bytes, B, H, T, D, 1, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(dq=None), -1), (dict(ws=None), -1), (dict(T=0), -1), (dict(B=0), -1),
+    (dict(D=128), -2), (dict(dtype=0), -2), (dict(dtype=5), -1),
+    (dict(scale=math.nan), -1), (dict(scale=3e38), -1),
+    (dict(q=FAKE + 8), -1), (dict(dq=FAKE + 2), -1), (dict(ws=FAKE + 4), -1),
+    (dict(lse=FAKE + 2), -1), (dict(ws_bytes=16), -1),
+    (dict(B=4096, H=2048, T=256), -2),  # grid beyond one launch
+    (dict(T=1 << 25), -2),  # one slice over 4 GiB
+])
+def test_bwd_rejects_invalid(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_and_flops():
+    for B, H, T in [(1, 1, 1), (2, 3, 1000), (4, 12, 8192)]:
+        assert osa.attn_bwd_workspace_bytes(B, H, T) == -(-B * H * T * 4 // 256) * 256
+    assert osa.attn_bwd_workspace_bytes(0, 1, 1) == 0
+    assert osa.attn_bwd_workspace_bytes(1 << 30, 1 << 30, 1 << 30) == 0
+    # five products to the forward's two
+    assert osa.attn_bwd_flops(4, 12, 8192, 64, True) == 5.0 * 4 * 12 * 8192 ** 2 * 64
+    assert osa.attn_bwd_flops(1, 1, 10, 64, False) == 2.5 * 4 * 100 * 64
+
+
 def test_naive_workspace_bytes():
     for B, H, T in [(1, 1, 256), (1, 1, 4096), (2, 3, 1000), (1, 1, 1)]:
         want = (2 * B * H * T * T + B * H * T) * 4
@@ -177,7 +207,7 @@ def test_traffic_rejects_invalid(lib):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 9
+    assert n == 19
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None
