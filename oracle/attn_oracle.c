@@ -197,13 +197,14 @@ int oracle_probabilities(const float* q, const float* k, int64_t T, int64_t D,
 }
 
 /* s_ij = scale * q_i . k_j, P_ij = exp(s_ij - lse_i), dP_ij = dO_i . v_j and
- * dS_ij = P_ij * (dP_ij - delta_i) for one visible pair of one slice (q, k,
- * v, dout: float32 [T, D] of the slice). */
+ * dS_ij = P_ij * (dP_ij - delta_i) for one visible pair (i, j < T) of one
+ * slice (q, k, v, dout: float32 [T, D] of the slice). */
 static void oracle_pair(const float* q, const float* k, const float* v,
-                        const float* dout, int64_t D, double scale,
+                        const float* dout, int64_t T, int64_t D, double scale,
                         const double* lse, const double* delta, int64_t i,
                         int64_t j, double* P, double* dS) {
     double dot = 0.0, dpv = 0.0;
+    (void)T;
     for (int64_t e = 0; e < D; ++e) dot += (double)q[i * D + e] * (double)k[j * D + e];
     for (int64_t e = 0; e < D; ++e) dpv += (double)dout[i * D + e] * (double)v[j * D + e];
     *P = exp(scale * dot - lse[i]);
@@ -298,7 +299,7 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
             for (int64_t e = 0; e < D; ++e) g[e] = 0.0;
             for (int64_t j = 0; j < visible; ++j) {
                 double P, dS;
-                oracle_pair(qs, ks, vs, ds, D, scale, lse, delta, i, j, &P, &dS);
+                oracle_pair(qs, ks, vs, ds, T, D, scale, lse, delta, i, j, &P, &dS);
                 for (int64_t e = 0; e < D; ++e) g[e] += dS * (double)ks[j * D + e];
             }
             for (int64_t e = 0; e < D; ++e) g[e] *= scale;
@@ -315,7 +316,7 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
             for (int64_t e = 0; e < D; ++e) gk[e] = gv[e] = 0.0;
             for (int64_t i = causal ? j : 0; i < T; ++i) {
                 double P, dS;
-                oracle_pair(qs, ks, vs, ds, D, scale, lse, delta, i, j, &P, &dS);
+                oracle_pair(qs, ks, vs, ds, T, D, scale, lse, delta, i, j, &P, &dS);
                 for (int64_t e = 0; e < D; ++e) {
                     gk[e] += dS * (double)qs[i * D + e];
                     gv[e] += P * (double)ds[i * D + e];
