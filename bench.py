@@ -38,7 +38,7 @@ BF16_TOL, F32_TOL_BASE = 2e-2, 1e-5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "fused_bf16_causal_b4h12_t8192_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "online_softmax_amd", "csrc", f)
-                  for f in ("fused_fwd.hip", "fused_layout.h")]
+                  for f in ("fused_fwd.hip", "fused_layout.h", "gfx950.h")]
 
 
 def log(*a):
@@ -165,6 +165,84 @@ def time_fused(osa, torch, q, k, v, o, lse, w, steps, warmup):
     return wall * 1e3 / steps, ms
 
 
+def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
+                 warmup=3, with_oracle=True):
+    """The backward pass (attn_bwd_stream) on the same workload for a seeded
+    output gradient: a correctness gate against the double oracle on one
+    whole slice (also the backward's CPU baseline), then HIP-event timing.
+    Throughput uses the pages' count for the pass, five products to the
+    forward's two ("Flash attention in PyTorch, then in Triton", section
+    "Backwards, and training with it"); the two-kernel split performs seven."""
+    import numpy as np
+    from online_softmax_amd.inputs import make_qkv
+    dev = qd.device
+    (dout,) = make_qkv(w.B, w.H, w.T, w.D, w.dtype, w.seed + 7)[:1]
+    dd = dout.to(dev)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(osa.attn_bwd_workspace_bytes(w.B, w.H, w.T), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: osa.attn_bwd_stream(qd, kd, vd, o, dd, lse, dq, dk, dv, ws,
+                                      w.causal, w.scale, stream)
+    run()
+    torch.cuda.synchronize()
+    out = {"kernels": ["bwd_delta16", "bwd_kv16", "bwd_q16"]}
+    flops = osa.attn_bwd_flops(w.B, w.H, w.T, w.D, w.causal)
+    if with_oracle:
+        sl = np.array([0])
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        want = oracle.attention_backward(q, k, v, dout, w.causal, w.scale, slices=sl,
+                                         threads=threads)
+        dt = time.perf_counter() - t0
+        errs, ok = {}, True
+        for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+            got = g.float().cpu().numpy().reshape(w.B * w.H, w.T, w.D)[sl]
+            bound = 2e-2 * max(1.0, float(np.abs(ref).max()))
+            e = float(np.abs(got - ref).max())
+            fin = bool(np.isfinite(got).all())
+            errs[name] = {"max_abs_err": e, "bound": bound, "finite": fin}
+            ok = ok and fin and e <= bound
+        out["parity"] = {"slices": sl.tolist(), "grads": errs, "pass": ok}
+        slice_flops = flops / (w.B * w.H)
+        out["cpu_baseline"] = {
+            "value": slice_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"gradients of slice 0 (of {w.B * w.H}) of {w.name}, "
+                       f"{slice_flops:.3e} flop by the pages' count in {dt:.2f} s "
+                       f"on {threads} threads of {cpu_model()}")}
+        log(f"backward parity on slice 0: {errs}")
+        if not ok:
+            log("backward correctness gate FAILED: not timing it")
+            out["pass"] = False
+            return out
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean = statistics.fmean(ms)
+    achieved = flops / (mean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    out.update({
+        "ms": {"mean": mean, "median": statistics.median(ms), "min": min(ms)},
+        "flop_convention": flops, "flop_performed": flops * 7.0 / 5.0,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "achieved_performed": achieved * 7.0 / 5.0},
+        "pass": True})
+    log(f"backward: mean {mean:.4f} ms, {achieved:.1f} TFLOP/s by the pages' count "
+        f"({achieved * 1.4:.1f} performed) = {100 * achieved / peak:.1f}% of {peak}")
+    del dq, dk, dv, ws, dd
+    return out
+
+
 def contrast(osa, torch, oracle, steps=10):
     """Both paths on the fp32 single-head workloads of the page
     "attention.cu" (bytes first, then a correctness gate, then time)."""
@@ -234,6 +312,8 @@ def main():
                     help="oracle sample size for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contrast", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB "
                          "(reference kernel for PMC byte counters)")
@@ -305,6 +385,12 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {a.copy_mib} MiB x 3 (PMC reference)")
 
+    bwd = None
+    if not a.no_backward and w.dtype != "f32":
+        import oracle
+        bwd = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
+                           with_oracle=not a.no_cpu_baseline)
+
     extra = None
     if not a.no_contrast:
         import oracle
@@ -334,6 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "kernels": kernels,
+        "backward": bwd,
         "contrast_fp32_single_head": extra,
         "kernel_source_sha256": kernel_source_hash(),
     }
