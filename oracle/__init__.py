@@ -69,6 +69,11 @@ def _load():
             g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                           ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                           ctypes.c_void_p]
+            d = lib.oracle_attention_kv
+            d.restype = ctypes.c_int
+            d.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [
+                ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int]
             b = lib.oracle_attention_backward
             b.restype = ctypes.c_int
             b.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
@@ -190,3 +195,26 @@ def attention_backward(q, k, v, dout, causal: bool, scale: float,
     if single and slices is None:
         return dq[0, 0], dk[0, 0], dv[0, 0]
     return dq, dk, dv
+
+
+def attention_kv(q, k, v, causal: bool, scale: float, threads: int = 0):
+    """Exact attention of Tq new queries against a Tk-token key/value cache
+    (decode), in double precision: q [B, H, Tq, D], k and v [B, H, Tk, D],
+    Tq <= Tk; query i sits at position Tk - Tq + i, so the causal mask is
+    aligned to the bottom-right of the table. Returns (o [B, H, Tq, D],
+    lse [B, H, Tq]) as float64."""
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B, H, Tq, D] and k, v [B, H, Tk, D] expected")
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    o = np.empty((B, H, Tq, D), np.float64)
+    lse = np.empty((B, H, Tq), np.float64)
+    rc = _load().oracle_attention_kv(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                     B, H, Tq, Tk, D, int(bool(causal)),
+                                     float(scale), o.ctypes.data,
+                                     lse.ctypes.data, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_kv failed (%d)" % rc)
+    return o, lse

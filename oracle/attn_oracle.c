@@ -166,6 +166,55 @@ int oracle_attention(const float* q, const float* k, const float* v,
 }
 
 /*
+ * Attention of a few new queries against a key/value cache (decode): q is
+ * float32 [B, H, Tq, D], k and v are float32 [B, H, Tk, D] with Tq <= Tk.
+ * Query i is the token at position Tk - Tq + i of the sequence the cache
+ * holds, so with causal != 0 it sees keys 0 .. Tk - Tq + i (the mask aligned
+ * to the bottom-right of the Tq x Tk table); otherwise every key. The page
+ * "Flash attention in PyTorch, then in Triton" names this case (new tokens
+ * against all the keys, section "Backwards, and training with it") as one
+ * its kernel does not handle. Each row is oracle_one_row at that position.
+ * o: double [B*H*Tq, D]; lse: double [B*H*Tq] or NULL. Returns 0, -1 on
+ * invalid arguments, -2 when scratch memory could not be allocated.
+ */
+int oracle_attention_kv(const float* q, const float* k, const float* v,
+                        int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
+                        int causal, double scale, double* o, double* lse,
+                        int nthreads) {
+    if (!q || !k || !v || !o || B < 1 || H < 1 || Tq < 1 || Tk < Tq || D < 1)
+        return -1;
+    const int64_t n = B * H * Tq;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double* scratch = (double*)malloc((size_t)Tk * sizeof(double));
+        if (!scratch) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            bad = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t r = 0; r < n; ++r) {
+            if (!scratch) continue;
+            const int64_t slice = r / Tq;
+            const int64_t i = r % Tq;
+            oracle_one_row(q + r * D, k + slice * Tk * D, v + slice * Tk * D, Tk, D,
+                           causal, scale, Tk - Tq + i, scratch, o + r * D,
+                           lse ? lse + r : NULL);
+        }
+        free(scratch);
+    }
+    (void)nthreads;
+    return bad ? -2 : 0;
+}
+
+/*
  * The full probability table of one head, for tiny shapes: P[i, j] is the
  * softmax weight of key j for query i (0 for a masked key). q, k: float32
  * [T, D]; P: double [T, T]. Same arithmetic as oracle_one_row.

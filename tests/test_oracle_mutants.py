@@ -61,8 +61,20 @@ BACKWARD_MUTANTS = [
                                 "d += (double)ds[i * D + e] * (double)vs[i * D + e];")]),
 ]
 
+# mistakes in the decode alignment, checked against the decode pins
+DECODE_MUTANTS = [
+    ("kv_top_left", [("causal, scale, Tk - Tq + i, scratch", "causal, scale, i, scratch")]),
+    ("kv_one_early", [("causal, scale, Tk - Tq + i, scratch",
+                       "causal, scale, Tk - Tq + i - (i > 0), scratch")]),
+    ("kv_one_late", [("causal, scale, Tk - Tq + i, scratch",
+                      "causal, scale, (Tk - Tq + i + 1 < Tk ? Tk - Tq + i + 1 : Tk - 1), scratch")]),
+    ("kv_wrong_slice", [("k + slice * Tk * D, v + slice * Tk * D",
+                         "k + slice * Tq * D, v + slice * Tq * D")]),
+]
+
 CASES = [(n, e, "test_oracle_pins.py") for n, e in MUTANTS] + \
-    [(n, e, "test_oracle_bwd_pins.py") for n, e in BACKWARD_MUTANTS]
+    [(n, e, "test_oracle_bwd_pins.py") for n, e in BACKWARD_MUTANTS] + \
+    [(n, e, "test_oracle_kv_pins.py") for n, e in DECODE_MUTANTS]
 
 
 @pytest.mark.parametrize("name,edits,pins", CASES, ids=[c[0] for c in CASES])
