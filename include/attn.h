@@ -153,6 +153,40 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
  * for sizes < 1 or when the count overflows 64 bits. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T);
 
+/*
+ * attn_decode_stream - attention of Tq new queries against a key/value cache
+ * of Tk tokens (decode). Query i is the token at position Tk - Tq + i, so
+ * with causal != 0 it sees keys 0 .. Tk - Tq + i (the mask aligned to the
+ * bottom-right of the Tq x Tk table); otherwise every key. "Flash attention
+ * in PyTorch, then in Triton" (section "Backwards, and training with it")
+ * names this case as one its kernel does not handle.
+ *
+ * q         : device, [B, H, Tq, D] of `dtype`, read only.
+ * k, v      : device, [B, H, Tk, D] of `dtype`, read only (the cache).
+ * o         : device, [B, H, Tq, D] of `dtype`, written.
+ * lse       : device, float32 [B, H, Tq] (natural log), written; may be NULL.
+ * workspace : caller-owned device buffer of at least
+ *             attn_decode_workspace_bytes(B, H, Tq, Tk) bytes (16-byte
+ *             aligned) for the per-split partial results; contents undefined
+ *             afterwards.
+ * Tq, Tk    : 1 <= Tq <= Tk. D must be 64. scale, stream as attn_fwd_stream.
+ * dtype     : ATTN_BF16 or ATTN_F16; ATTN_F32 returns ATTN_ERR_UNSUPPORTED.
+ *
+ * The keys are split over workgroups and the partial results merged with the
+ * log-sum-exp identity O = sum_s exp(lse_s - lse) O_s. Returns ATTN_OK once
+ * enqueued, or an error status with nothing enqueued (ATTN_ERR_INVALID for a
+ * null or misaligned pointer, Tq > Tk, a bad size, dtype or scale, a short
+ * workspace; ATTN_ERR_UNSUPPORTED for D != 64, float32, or sizes beyond one
+ * launch or a 4 GiB slice).
+ */
+int attn_decode_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Tq,
+                       int Tk, int D, int causal, float scale, int dtype, void* stream);
+
+/* Workspace bytes attn_decode_stream needs for these sizes (the split is
+ * chosen from them); 0 for invalid sizes or on overflow. */
+size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk);
+
 /* Arithmetic convention for the backward pass: five products to the
  * forward's two (dP, dV, dQ, dK and the recomputed scores), so 2.5 times
  * attn_flops ("Flash attention in PyTorch, then in Triton", section

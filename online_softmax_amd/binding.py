@@ -24,7 +24,8 @@ ATTN_PATH_FUSED, ATTN_PATH_NAIVE = 0, 1
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
            "attn_naive_workspace_bytes", "attn_bwd_stream",
-           "attn_bwd_workspace_bytes", "attn_bwd_flops", "attn_traffic_bytes",
+           "attn_bwd_workspace_bytes", "attn_bwd_flops", "attn_decode_stream",
+           "attn_decode_workspace_bytes", "attn_traffic_bytes",
            "attn_flops", "attn_status_string", "attn_last_hip_error",
            "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
            "attn_fused_tile")
@@ -79,6 +80,9 @@ def load(path: str = LIBRARY):
         lib.attn_bwd_workspace_bytes.restype = S
         lib.attn_bwd_flops.argtypes = [I, I, I, I, I]
         lib.attn_bwd_flops.restype = ctypes.c_double
+        lib.attn_decode_stream.argtypes = [P] * 6 + [S, I, I, I, I, I, I, F, I, P]
+        lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
+        lib.attn_decode_workspace_bytes.restype = S
         lib.attn_traffic_bytes.argtypes = [I, I, I, I, I, I, I,
                                            ctypes.POINTER(attn_traffic)]
         lib.attn_flops.argtypes = [I, I, I, I, I]
@@ -189,6 +193,24 @@ def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
     _check(st, "attn_bwd_stream")
 
 
+def attn_decode_workspace_bytes(B: int, H: int, Tq: int, Tk: int) -> int:
+    return int(_lib().attn_decode_workspace_bytes(B, H, Tq, Tk))
+
+
+def attn_decode_stream(q, k, v, o, lse, workspace, causal: bool, scale: float,
+                       stream=None):
+    """Decode: q [B, H, Tq, D] against the cache k, v [B, H, Tk, D] into o
+    (q's shape) and lse ([B, H, Tq] float32 or None)."""
+    B, H, Tq, D = _dims(q)
+    Tk = int(k.shape[2])
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib().attn_decode_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(workspace), nbytes, B, H, Tq, Tk, D,
+                                   int(bool(causal)), float(scale), dtype_code(q),
+                                   _stream(stream, q.device))
+    _check(st, "attn_decode_stream")
+
+
 def attn_bwd_flops(B: int, H: int, T: int, D: int, causal: bool) -> float:
     return float(_lib().attn_bwd_flops(B, H, T, D, int(bool(causal))))
 
@@ -266,3 +288,20 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = True,
                      device=q.device)
     attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
     return dq, dk, dv
+
+
+def attention_decode(q, k, v, causal: bool = True, scale: float | None = None,
+                     stream=None):
+    """Allocate o, lse and the workspace with torch and run the decode path.
+    Returns (o, lse)."""
+    import torch
+    B, H, Tq, D = _dims(q)
+    Tk = int(k.shape[2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(attn_decode_workspace_bytes(B, H, Tq, Tk), dtype=torch.uint8,
+                     device=q.device)
+    attn_decode_stream(q, k, v, o, lse, ws, causal, scale, stream)
+    return o, lse

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "fused_fwd.hip", "naive_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.hip", "fused_fwd.hip", "naive_fwd.hip", "attn_bwd.hip",
+           "attn_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -135,6 +135,58 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
     return ATTN_OK;
 }
 
+size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk) {
+    if (B < 1 || H < 1 || Tq < 1 || Tk < Tq) return 0;
+    uint64_t bh, rows;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || bh > (uint64_t)INT32_MAX) return 0;
+    if (!mul_ok(bh, (uint64_t)Tq, &rows)) return 0;
+    int nsplit, chunk;
+    attn::decode_plan((int)bh, Tq, Tk, &nsplit, &chunk);
+    uint64_t parts, bytes;
+    if (!mul_ok(rows, (uint64_t)nsplit, &parts)) return 0;
+    if (!mul_ok(parts, (uint64_t)(attn::kHeadDim + 1) * 4, &bytes)) return 0;
+    if (bytes > UINT64_MAX - 1024) return 0;
+    return (size_t)((bytes + 256 + 255) & ~(uint64_t)255);
+}
+
+int attn_decode_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Tq,
+                       int Tk, int D, int causal, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID;
+    if (B < 1 || H < 1 || Tq < 1 || Tk < 1 || D < 1) return ATTN_ERR_INVALID;
+    if (Tq > Tk) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, Tk, D);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(workspace))
+        return ATTN_ERR_INVALID;
+    if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
+    const size_t need = attn_decode_workspace_bytes(B, H, Tq, Tk);
+    if (need == 0) return ATTN_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return ATTN_ERR_INVALID;
+    if ((uint64_t)Tk * D * 2 > UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    int nsplit, chunk;
+    const int BH = B * H;
+    attn::decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    const uint64_t nqt = ((uint64_t)Tq + 31) / 32;
+    if ((uint64_t)BH * nqt * nsplit > kMaxFusedWorkgroups ||
+        ((uint64_t)BH * Tq + 3) / 4 > (uint64_t)INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
+    const double c = fabs((double)scale) * 1.4426950408889634073599;
+    if (!isfinite((float)c)) return ATTN_ERR_INVALID;
+    const uint64_t parts = (uint64_t)BH * Tq * nsplit;
+    float* o_part = (float*)workspace;
+    float* lse_part = o_part + parts * attn::kHeadDim;
+    const hipError_t e = attn::launch_decode(q, k, v, o, lse, o_part, lse_part, BH, Tq, Tk,
+                                             causal ? 1 : 0, (float)c, scale < 0.0f, dtype,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
 double attn_bwd_flops(int B, int H, int T, int D, int causal) {
     return 2.5 * attn_flops(B, H, T, D, causal);
 }
@@ -254,7 +306,8 @@ const char* attn_status_string(int status) {
 int attn_last_hip_error(void) { return g_last_hip_error; }
 
 int attn_kernel_count(void) {
-    return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels;
+    return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
+           attn::kDecodeKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -268,7 +321,10 @@ const char* attn_kernel_name(int kernel) {
         "bwd_kv16<bf16, full>",      "bwd_q16<bf16, causal>",
         "bwd_q16<bf16, full>",       "bwd_delta16<f16>",
         "bwd_kv16<f16, causal>",     "bwd_kv16<f16, full>",
-        "bwd_q16<f16, causal>",      "bwd_q16<f16, full>"};
+        "bwd_q16<f16, causal>",      "bwd_q16<f16, full>",
+        "decode_split16<bf16, causal>", "decode_split16<bf16, full>",
+        "decode_combine16<bf16>",    "decode_split16<f16, causal>",
+        "decode_split16<f16, full>", "decode_combine16<f16>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -277,9 +333,11 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     if (!out || kernel < 0 || kernel >= attn_kernel_count())
         return ATTN_ERR_INVALID;
     const int naive0 = attn::kFusedKernels, bwd0 = naive0 + attn::kNaiveKernels;
+    const int dec0 = bwd0 + attn::kBwdKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
-                                     : attn::bwd_kernel_ptr(kernel - bwd0);
+                     : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
+                                     : attn::decode_kernel_ptr(kernel - dec0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);

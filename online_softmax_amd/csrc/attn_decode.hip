@@ -1,0 +1,309 @@
+// Attention of a few new queries against a key/value cache (decode) for
+// gfx950: Tq queries, Tk cached keys and values per (batch, head) slice,
+// query i standing at position Tk - Tq + i, so the causal mask is aligned to
+// the bottom-right of the Tq x Tk table. "Flash attention in PyTorch, then
+// in Triton" names this case (new tokens against all the keys, section
+// "Backwards, and training with it") as one its kernel does not handle.
+//
+// With few queries there is too little work per slice to fill the GPU along
+// the queries, so the keys are split: decode_split16 gives every workgroup
+// one query tile (32 rows) and one range of keys, and writes a partial
+// result normalised by its own denominator together with its log-sum-exp;
+// decode_combine16 then merges the partials of a row with the same identity
+// the online softmax uses between key tiles: with lse = log sum_s exp(lse_s),
+// O = sum_s exp(lse_s - lse) O_s.
+//
+// Inside a workgroup each of the 4 waves takes every fourth 32-key tile of
+// the range, streamed by direct buffer loads into an LDS ring of its own (no
+// barrier until the end), and keeps its own online-softmax state; S^T = K Q^T
+// and O^T += V^T P^T run on v_mfma_f32_32x32x16 exactly as in the forward
+// kernel (fused_fwd.hip), half-height K/V tiles. The four states are merged
+// through LDS at the end. The path moves the K/V cache once: it is bound by
+// HBM bandwidth.
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fused_layout.h"
+#include "gfx950.h"
+#include "kernels.h"
+
+namespace attn {
+
+constexpr float kDecLn2 = 0.693147180559945309417f;
+
+// One 32-key tile of K or V into `off` (4 wave instructions): rows from
+// row0, rows at or past `rows_end` fetch row rows_end - 1 (their weight is
+// masked to 0).
+__device__ inline void dec_load(v4u32_rsrc rs, const uint32_t (&voff)[4], int row0,
+                                int rows_end, uint32_t off) {
+    if (row0 + kDecTile <= rows_end) {
+        const uint32_t soff = (uint32_t)row0 * (kHeadDim * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(rs, voff[i], soff, off + 1024 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(row0 + (int)(voff[i] >> 7), rows_end - 1);
+            dma16(rs, (uint32_t)r * (kHeadDim * 2) + (voff[i] & 127), 0u, off + 1024 * i);
+        }
+    }
+}
+
+// Partial results of one split: o_part [rows, nsplit, 64] float32 (normalised
+// by the split's own denominator), lse_part [rows, nsplit] (natural log; -inf
+// where the split holds no visible key of the row). rows = BH * Tq.
+template <int DT, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void decode_split16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
+    int Tq, int Tk, int nqt, int nsplit, int chunk, float c, uint32_t qsign) {
+    constexpr int kStages = 2;
+    __shared__ __attribute__((aligned(1024))) char ring[kWaves][kStages][2][kDecTileBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+
+    // block -> (slice, query tile, split); splits of one slice are adjacent
+    const int per_slice = nqt * nsplit;
+    const int bh = blockIdx.x / per_slice;
+    const int rem = blockIdx.x - bh * per_slice;
+    const int qt = rem / nsplit;
+    const int split = rem - qt * nsplit;
+    const int my_q = qt * kDecTile + ql;  // this lane's query (0 .. Tq-1 valid)
+
+    // keys this split covers, cut at the last key any query of the tile sees
+    const int last_q = min(qt * kDecTile + kDecTile - 1, Tq - 1);
+    const int kend_all = CAUSAL ? (Tk - Tq + last_q + 1) : Tk;
+    const int k_begin = split * chunk;
+    const int k_end = min(k_begin + chunk, kend_all);
+    // this lane's first invisible key
+    const int limit = min(k_end, CAUSAL ? (Tk - Tq + my_q + 1) : Tk);
+
+    v4u32 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        v4u32 x = {0u, 0u, 0u, 0u};
+        if (my_q < Tq)
+            x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * kHeadDim + q_col16(hh, ks));
+        qf[ks] = x ^ qsign;
+    }
+    wait_vmcnt<0>();
+
+    const uint32_t slice_bytes = (uint32_t)Tk * (kHeadDim * 2);
+    const int64_t kv_base = (int64_t)bh * Tk * kHeadDim;
+    const v4u32_rsrc krs = buffer_rsrc(k + kv_base, slice_bytes);
+    const v4u32_rsrc vrs = buffer_rsrc(v + kv_base, slice_bytes);
+    uint32_t kvoff[4], vvoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kvoff[i] = (uint32_t)dl_global_byte(i >> 1, i & 1, lane, false);
+        vvoff[i] = (uint32_t)dl_global_byte(i >> 1, i & 1, lane, true);
+    }
+    // this wave's tiles: k_begin + 32 * (wave + 4 t), t = 0 .. n - 1
+    const int ntile_all = k_end > k_begin ? (k_end - k_begin + kDecTile - 1) / kDecTile : 0;
+    const int n = ntile_all > wave ? (ntile_all - wave + kWaves - 1) / kWaves : 0;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
+    auto issue = [&](int t) {
+        const int k0 = k_begin + kDecTile * (wave_u + kWaves * t);
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)ring[wave_u][t % kStages][0];
+        dec_load(krs, kvoff, k0, k_end, base);
+        dec_load(vrs, vvoff, k0, k_end, base + kDecTileBytes);
+    };
+
+    // lane bases of the fragment reads (the swizzles depend on the lane only)
+    uint32_t ko[4], vo[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ko[ks] = (uint32_t)kfrag_byte(ql, hh, 0, ks);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) vo[mt] = (uint32_t)vtr_byte(lane, mt, 0, 0);
+
+    v16f32 oacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
+    float m = -FLT_MAX, mc = -FLT_MAX * c, l = 0.f;
+
+    if (n >= 1) issue(0);
+    for (int t = 0; t < n; ++t) {
+        if (t + 1 < n) {
+            issue(t + 1);
+            wait_vmcnt<8>();  // tile t landed, tile t+1 in flight
+        } else {
+            wait_vmcnt<0>();
+        }
+        const char* kb = ring[wave][t % kStages][0];
+        const char* vb = ring[wave][t % kStages][1];
+        const int k0 = k_begin + kDecTile * (wave + kWaves * t);
+        // S^T = K Q^T (32 keys x 32 queries)
+        v16f32 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            s = mfma16<DT>(*(const v4u32*)(kb + ko[ks]), qf[ks], s);
+        // mask, running maximum, rescale
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (k0 + acc_row(r, hh) >= limit) s[r] = -INFINITY;
+            mx = fmaxf(mx, s[r]);
+        }
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m, mx);
+        const float mc_new = m_new * c;
+        const float corr = fast_exp2(mc - mc_new);
+        m = m_new;
+        mc = mc_new;
+        l *= corr;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
+        // weights of the tile's 32 keys: P fragments of two 16-key steps
+        v4u32 pf[2];
+        float t0 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 8 * ks + 2 * i;
+                float p0 = fast_exp2(fmaf(s[r], c, -mc));
+                float p1 = fast_exp2(fmaf(s[r + 1], c, -mc));
+                if (s[r] == -INFINITY) p0 = 0.f;
+                if (s[r + 1] == -INFINITY) p1 = 0.f;
+                pf[ks][i] = pack2<DT>(p0, p1);
+                t0 = sum2<DT>(pf[ks][i], t0);
+            }
+        l += t0;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+                const char* p = vb + vo[mt] + kVtrKsStride * ks;
+                const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+                const v4i16 b =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + kVtrHalfStride));
+                const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
+                oacc[mt] = mfma16<DT>((v4u32){a2[0], a2[1], b2[0], b2[1]}, pf[ks], oacc[mt]);
+            }
+    }
+
+    // merge the four waves' states through LDS (the ring is free now)
+    __syncthreads();
+    float* so = (float*)&ring[0][0][0][0];      // [wave][32 queries][64 dims]
+    float* sm = so + kWaves * kDecTile * kHeadDim;  // [wave][32] reference mc
+    float* sl = sm + kWaves * kDecTile;             // [wave][32] denominator
+    const float lt = halves_sum(l);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            so[(wave * kDecTile + ql) * kHeadDim + 32 * mt + acc_row(r, hh)] = oacc[mt][r];
+    if (hh == 0) {
+        sm[wave * kDecTile + ql] = mc;
+        sl[wave * kDecTile + ql] = lt;
+    }
+    __syncthreads();
+    // thread -> (query row, 8 dims)
+    const int rq = tid >> 3, d0 = 8 * (tid & 7);
+    const int qrow = qt * kDecTile + rq;
+    if (qrow < Tq) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            if (sl[w * kDecTile + rq] > 0.f) M = fmaxf(M, sm[w * kDecTile + rq]);
+        float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float lw = sl[w * kDecTile + rq];
+                if (!(lw > 0.f)) continue;
+                const float e = fast_exp2(sm[w * kDecTile + rq] - M);
+                L += e * lw;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] += e * so[(w * kDecTile + rq) * kHeadDim + d0 + j];
+            }
+        }
+        const int64_t p = ((int64_t)bh * Tq + qrow) * nsplit + split;
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o_part[p * kHeadDim + d0 + j] = acc[j] * inv;
+        if ((tid & 7) == 0) lse_part[p] = L > 0.f ? (M + log2f(L)) * kDecLn2 : -INFINITY;
+    }
+}
+
+// Merge the nsplit partials of every row: one wave per row, a lane per dim.
+template <int DT>
+__global__ __launch_bounds__(256) void decode_combine16(const float* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part,
+                                                        uint16_t* __restrict__ o,
+                                                        float* __restrict__ lse, int64_t rows,
+                                                        int nsplit) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int d = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float* lp = lse_part + row * nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+    float L = 0.f, acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        if (lp[s] == -INFINITY) continue;
+        const float e = __expf(lp[s] - M);
+        L += e;
+        acc += e * o_part[(row * nsplit + s) * kHeadDim + d];
+    }
+    const float val = acc / L;
+    o[row * kHeadDim + d] = (uint16_t)(pack2<DT>(val, 0.f) & 0xffffu);
+    if (d == 0 && lse != nullptr) lse[row] = M + logf(L);
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                         float* o_part, float* lse_part, int BH, int Tq, int Tk,
+                         int causal, float c, bool negate_q, int dt, hipStream_t stream) {
+    int nsplit, chunk;
+    decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    const int nqt = (Tq + kDecTile - 1) / kDecTile;
+    const uint32_t sign = negate_q ? 0x80008000u : 0u;
+    const dim3 grid((unsigned)(BH * nqt * nsplit));
+    const int64_t rows = (int64_t)BH * Tq;
+    const dim3 cgrid((unsigned)((rows + 3) / 4));
+    const uint16_t* q16 = (const uint16_t*)q;
+    const uint16_t* k16 = (const uint16_t*)k;
+    const uint16_t* v16 = (const uint16_t*)v;
+    if (dt == ATTN_DT_BF16) {
+        auto fn = causal ? decode_split16<ATTN_DT_BF16, true> : decode_split16<ATTN_DT_BF16, false>;
+        hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q16, k16, v16, o_part,
+                           lse_part, Tq, Tk, nqt, nsplit, chunk, c, sign);
+        hipLaunchKernelGGL(decode_combine16<ATTN_DT_BF16>, cgrid, dim3(256), 0, stream,
+                           o_part, lse_part, (uint16_t*)o, lse, rows, nsplit);
+    } else {
+        auto fn = causal ? decode_split16<ATTN_DT_F16, true> : decode_split16<ATTN_DT_F16, false>;
+        hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q16, k16, v16, o_part,
+                           lse_part, Tq, Tk, nqt, nsplit, chunk, c, sign);
+        hipLaunchKernelGGL(decode_combine16<ATTN_DT_F16>, cgrid, dim3(256), 0, stream,
+                           o_part, lse_part, (uint16_t*)o, lse, rows, nsplit);
+    }
+    return hipGetLastError();
+}
+
+const void* decode_kernel_ptr(int index) {
+    switch (index) {
+        case 0: return (const void*)decode_split16<ATTN_DT_BF16, true>;
+        case 1: return (const void*)decode_split16<ATTN_DT_BF16, false>;
+        case 2: return (const void*)decode_combine16<ATTN_DT_BF16>;
+        case 3: return (const void*)decode_split16<ATTN_DT_F16, true>;
+        case 4: return (const void*)decode_split16<ATTN_DT_F16, false>;
+        case 5: return (const void*)decode_combine16<ATTN_DT_F16>;
+        default: return nullptr;
+    }
+}
+
+}  // namespace attn

@@ -249,6 +249,25 @@ ATTN_HD int bwd_first_qtile(int kb, bool causal) {
     return causal ? (kb * kBwdBlockKV) / kBwdBlockQ : 0;
 }
 
+// ---- decode (few queries against a key/value cache) -------------------------
+// A workgroup takes one tile of kDecTile queries and one chunk of keys; its 4
+// waves take every fourth 32-key tile of the chunk. The chunk is chosen so
+// that about 2048 workgroups fill the GPU, a multiple of 4 waves x 32 keys.
+constexpr int kDecTile = 32;                             // keys per tile, queries per tile
+constexpr int kDecTileBytes = kDecTile * kHeadDim * 2;   // 4 KiB
+ATTN_HD void decode_plan(int BH, int Tq, int Tk, int* nsplit, int* chunk) {
+    const int nqt = (Tq + kDecTile - 1) / kDecTile;
+    const long long base = (long long)BH * nqt;
+    long long want = (2048 + base - 1) / base;
+    const int max_split = (Tk + kWaves * kDecTile - 1) / (kWaves * kDecTile);
+    if (want > max_split) want = max_split;
+    if (want < 1) want = 1;
+    int ch = (int)((Tk + want - 1) / want);
+    ch = (ch + kWaves * kDecTile - 1) / (kWaves * kDecTile) * (kWaves * kDecTile);
+    *chunk = ch;
+    *nsplit = (Tk + ch - 1) / ch;
+}
+
 // Q fragment of lane-half h for reduction step ks: dims 16*ks + 8*h .. +7.
 ATTN_HD int q_col16(int h, int ks) { return 16 * ks + 8 * h; }
 

@@ -32,12 +32,21 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       float* delta, int BH, int T, int causal, float c, float scale,
                       bool negate, int dt, hipStream_t stream);
 
+// Decode: Tq queries against a Tk-token cache, split over the keys into
+// o_part [BH*Tq, nsplit, 64] and lse_part [BH*Tq, nsplit] (float32), then
+// merged; the split is decode_plan (fused_layout.h).
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                         float* o_part, float* lse_part, int BH, int Tq, int Tk,
+                         int causal, float c, bool negate_q, int dt, hipStream_t stream);
+
 // Kernel table for attribute queries.
 constexpr int kFusedKernels = 6;
 constexpr int kNaiveKernels = 3;
 constexpr int kBwdKernels = 10;
+constexpr int kDecodeKernels = 6;
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
+const void* decode_kernel_ptr(int index);
 
 }  // namespace attn

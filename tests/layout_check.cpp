@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <set>
+#include <algorithm>
 #include <vector>
 
 #include "fused_layout.h"
@@ -441,6 +442,65 @@ static void check_bwd_access(int BH, int T, bool causal) {
     }
 }
 
+// The decode kernels: every workgroup's key range, each wave's tile loads
+// (rows clamped below the range end, inside the slice), the LDS ring and the
+// merge area, and the partial-result indices.
+static void check_decode(int BH, int Tq, int Tk, bool causal) {
+    int nsplit, chunk;
+    decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    CHECK(nsplit >= 1 && chunk % (kWaves * kDecTile) == 0, "decode plan");
+    CHECK((long)nsplit * chunk >= Tk && (long)(nsplit - 1) * chunk < Tk, "decode split cover");
+    const int nqt = (Tq + kDecTile - 1) / kDecTile;
+    const long parts = (long)BH * Tq * nsplit;
+    const long ring_bytes = (long)kWaves * 2 * 2 * kDecTileBytes;
+    CHECK((long)kWaves * kDecTile * kHeadDim * 4 + 2 * kWaves * kDecTile * 4 <= ring_bytes,
+          "decode merge area exceeds the ring");
+    std::vector<int> covered((size_t)Tk, 0);
+    for (int b = 0; b < BH * nqt * nsplit; ++b) {
+        const int per = nqt * nsplit, bh = b / per, rem = b % per;
+        const int qt = rem / nsplit, split = rem % nsplit;
+        const int last_q = std::min(qt * kDecTile + kDecTile - 1, Tq - 1);
+        const int kend_all = causal ? (Tk - Tq + last_q + 1) : Tk;
+        const int k_begin = split * chunk;
+        const int k_end = std::min(k_begin + chunk, kend_all);
+        CHECK(kend_all >= 1 && kend_all <= Tk, "decode key end");
+        const int ntile = k_end > k_begin ? (k_end - k_begin + kDecTile - 1) / kDecTile : 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int n = ntile > w ? (ntile - w + kWaves - 1) / kWaves : 0;
+            for (int t = 0; t < n; ++t) {
+                const int k0 = k_begin + kDecTile * (w + kWaves * t);
+                CHECK(k0 < k_end, "decode tile past the range");
+                if (bh == 0 && qt == nqt - 1)
+                    for (int r = 0; r < kDecTile && k0 + r < k_end; ++r) covered[k0 + r]++;
+                for (int i = 0; i < 4; ++i)
+                    for (int l = 0; l < 64; ++l)
+                        for (int is_v = 0; is_v < 2; ++is_v) {
+                            const long voff = dl_global_byte(i >> 1, i & 1, l, is_v);
+                            long off;
+                            if (k0 + kDecTile <= k_end) {
+                                off = (long)k0 * 128 + voff;
+                            } else {
+                                long r = k0 + (voff >> 7);
+                                if (r > k_end - 1) r = k_end - 1;
+                                off = r * 128 + (voff & 127);
+                            }
+                            CHECK(off >= 0 && off + 16 <= (long)Tk * 128, "decode load outside slice");
+                            CHECK(1024 * i + 16 * l + 16 <= kDecTileBytes, "decode LDS tile");
+                        }
+            }
+        }
+        for (int rq = 0; rq < kDecTile; ++rq) {
+            const int qrow = qt * kDecTile + rq;
+            if (qrow >= Tq) continue;
+            const long p = ((long)bh * Tq + qrow) * nsplit + split;
+            CHECK(p >= 0 && p < parts, "decode partial index");
+        }
+    }
+    // the last query tile of a slice sees every key its queries may see, once
+    const int kend_last = causal ? Tk : Tk;
+    for (int j = 0; j < kend_last; ++j) CHECK(covered[j] == 1, "decode key %d covered %d times", j, covered[j]);
+}
+
 // The K / V rings of the 16-bit kernel: simulate one wave's issue order and
 // vmcnt waits (a wait leaving w loads in flight completes all older loads),
 // and check that each read finds its tile landed in its stage and that no
@@ -520,6 +580,11 @@ static void check_ring(int n, int n_main) {
 int main() {
     check_direct16();
     check_bwd_layout();
+    for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})
+        for (int Tq : {1, 2, 7, 31, 32, 33, 64, 100})
+            for (int BH : {1, 6, 48})
+                for (int causal = 0; causal < 2; ++causal)
+                    if (Tq <= Tk) check_decode(BH, Tq, Tk, causal);
     for (int T : {1, 63, 64, 65, 127, 128, 129, 300, 1000, 8192})
         for (int BH : {1, 6, 48})
             for (int causal = 0; causal < 2; ++causal) {

@@ -123,6 +123,33 @@ def test_bwd_workspace_and_flops():
     assert osa.attn_bwd_flops(1, 1, 10, 64, False) == 2.5 * 4 * 100 * 64
 
 
+def dec(lib, q=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1, H=1, Tq=1, Tk=8,
+        D=64, dtype=1, scale=0.125):
+    return lib.attn_decode_stream(q, FAKE, FAKE, FAKE, lse, ws, ws_bytes, B, H, Tq, Tk,
+                                  D, 1, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(ws=None), -1), (dict(Tq=0), -1), (dict(Tk=0), -1),
+    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=128), -2), (dict(dtype=0), -2),
+    (dict(dtype=9), -1), (dict(scale=math.inf), -1), (dict(q=FAKE + 8), -1),
+    (dict(ws=FAKE + 4), -1), (dict(lse=FAKE + 2), -1), (dict(ws_bytes=16), -1),
+    (dict(Tk=1 << 25), -2),  # one cache slice over 4 GiB
+])
+def test_decode_rejects_invalid(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_decode_workspace_bytes():
+    for B, H, Tq, Tk in [(1, 1, 1, 1), (4, 12, 1, 8192), (2, 3, 33, 1000)]:
+        n = osa.attn_decode_workspace_bytes(B, H, Tq, Tk)
+        assert n > 0 and n % 256 == 0
+        # at least one partial (64 floats + lse) per row
+        assert n >= B * H * Tq * 65 * 4
+    assert osa.attn_decode_workspace_bytes(1, 1, 5, 4) == 0
+    assert osa.attn_decode_workspace_bytes(0, 1, 1, 1) == 0
+
+
 def test_naive_workspace_bytes():
     for B, H, T in [(1, 1, 256), (1, 1, 4096), (2, 3, 1000), (1, 1, 1)]:
         want = (2 * B * H * T * T + B * H * T) * 4
@@ -207,7 +234,7 @@ def test_traffic_rejects_invalid(lib):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 19
+    assert n == 25
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None
