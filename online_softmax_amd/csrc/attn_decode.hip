@@ -84,16 +84,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
     // this lane's first invisible key
     const int limit = min(k_end, CAUSAL ? (Tk - Tq + my_q + 1) : Tk);
 
-    v4u32 qf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        v4u32 x = {0u, 0u, 0u, 0u};
-        if (my_q < Tq)
-            x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * kHeadDim + q_col16(hh, ks));
-        qf[ks] = x ^ qsign;
-    }
-    wait_vmcnt<0>();
-
     const uint32_t slice_bytes = (uint32_t)Tk * (kHeadDim * 2);
     const int64_t kv_base = (int64_t)bh * Tk * kHeadDim;
     const v4u32_rsrc krs = buffer_rsrc(k + kv_base, slice_bytes);
@@ -129,14 +119,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
     float m = -FLT_MAX, mc = -FLT_MAX * c, l = 0.f;
 
+    // the first two tiles, then the Q rows: the three latencies overlap (the
+    // compiler's wait for Q before its first use also covers the tiles)
     if (n >= 1) issue(0);
+    if (n >= 2) issue(1);
+    v4u32 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        v4u32 x = {0u, 0u, 0u, 0u};
+        if (my_q < Tq)
+            x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * kHeadDim + q_col16(hh, ks));
+        qf[ks] = x ^ qsign;
+    }
     for (int t = 0; t < n; ++t) {
-        if (t + 1 < n) {
-            issue(t + 1);
-            wait_vmcnt<8>();  // tile t landed, tile t+1 in flight
-        } else {
+        if (t + 1 < n)
+            wait_vmcnt<8>();  // tile t landed, tile t+1 (8 loads) in flight
+        else
             wait_vmcnt<0>();
-        }
         const char* kb = ring[wave][t % kStages][0];
         const char* vb = ring[wave][t % kStages][1];
         const int k0 = k_begin + kDecTile * (wave + kWaves * t);
@@ -194,6 +193,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
                 const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
                 oacc[mt] = mfma16<DT>((v4u32){a2[0], a2[1], b2[0], b2[1]}, pf[ks], oacc[mt]);
             }
+        // the stage of tile t is read (its fragments are in registers): refill
+        if (t + 2 < n) issue(t + 2);
     }
 
     // merge the four waves' states through LDS (the ring is free now)
@@ -240,29 +241,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
     }
 }
 
-// Merge the nsplit partials of every row: one wave per row, a lane per dim.
+// Merge the nsplit partials of every row: one wave per row. Lanes take the
+// splits' log-sum-exps (the maximum and the sum of the weights are wave
+// reductions), then a lane per dim accumulates the weighted partials, eight
+// independent loads at a time.
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
+    return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void decode_combine16(const float* __restrict__ o_part,
                                                         const float* __restrict__ lse_part,
                                                         uint16_t* __restrict__ o,
                                                         float* __restrict__ lse, int64_t rows,
                                                         int nsplit) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int d = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const float* lp = lse_part + row * nsplit;
+    const float* op = o_part + row * nsplit * kHeadDim + lane;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, lp[s]);
+    M = wave_max(M);
     float L = 0.f, acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        if (lp[s] == -INFINITY) continue;
-        const float e = __expf(lp[s] - M);
-        L += e;
-        acc += e * o_part[(row * nsplit + s) * kHeadDim + d];
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+        const int s = s0 + lane;
+        const float ls = s < nsplit ? lp[s] : -INFINITY;
+        const float e = ls == -INFINITY ? 0.f : __expf(ls - M);
+        L += wave_sum(e);
+        const int cnt = min(64, nsplit - s0);
+        const uint32_t eb = __builtin_bit_cast(uint32_t, e);
+#pragma unroll 8
+        for (int j = 0; j < cnt; ++j) {
+            const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
+            acc += ej * op[(int64_t)(s0 + j) * kHeadDim];
+        }
     }
     const float val = acc / L;
-    o[row * kHeadDim + d] = (uint16_t)(pack2<DT>(val, 0.f) & 0xffffu);
-    if (d == 0 && lse != nullptr) lse[row] = M + logf(L);
+    o[row * kHeadDim + lane] = (uint16_t)(pack2<DT>(val, 0.f) & 0xffffu);
+    if (lane == 0 && lse != nullptr) lse[row] = M + logf(L);
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse,

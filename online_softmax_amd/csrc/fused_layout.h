@@ -252,13 +252,14 @@ ATTN_HD int bwd_first_qtile(int kb, bool causal) {
 // ---- decode (few queries against a key/value cache) -------------------------
 // A workgroup takes one tile of kDecTile queries and one chunk of keys; its 4
 // waves take every fourth 32-key tile of the chunk. The chunk is chosen so
-// that about 2048 workgroups fill the GPU, a multiple of 4 waves x 32 keys.
+// that all workgroups run in one round, two per CU (512), a multiple of 4
+// waves x 32 keys: a workgroup's fixed start-up latency is paid once.
 constexpr int kDecTile = 32;                             // keys per tile, queries per tile
 constexpr int kDecTileBytes = kDecTile * kHeadDim * 2;   // 4 KiB
 ATTN_HD void decode_plan(int BH, int Tq, int Tk, int* nsplit, int* chunk) {
     const int nqt = (Tq + kDecTile - 1) / kDecTile;
     const long long base = (long long)BH * nqt;
-    long long want = (2048 + base - 1) / base;
+    long long want = 512 / base;
     const int max_split = (Tk + kWaves * kDecTile - 1) / (kWaves * kDecTile);
     if (want > max_split) want = max_split;
     if (want < 1) want = 1;
