@@ -243,6 +243,82 @@ def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
     return out
 
 
+def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps=20,
+               copies=4, with_oracle=True):
+    """The decode path (attn_decode_stream): Tq new tokens per sequence
+    against a Tk-token key/value cache, causal. It reads the cache once, so
+    it is bound by HBM: the figure is algorithmic bytes (K and V once, q and o
+    once) per call over the call's time, against 8 TB/s. Timed calls rotate
+    over `copies` caches, together larger than the 256 MB Infinity Cache, so
+    the reads reach HBM. A correctness gate against the double oracle on
+    every row comes first (also this leg's CPU baseline)."""
+    import numpy as np
+    from online_softmax_amd.inputs import make_qkv
+    dev = torch.device("cuda:0")
+    scale = 0.125
+    (q,) = make_qkv(B, H, Tq, 64, dtype, 2101)[:1]
+    caches = [make_qkv(B, H, Tk, 64, dtype, 2102 + i)[1:] for i in range(copies)]
+    qd = q.to(dev)
+    kv = [(k.to(dev), v.to(dev)) for k, v in caches]
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    ws = torch.empty(osa.attn_decode_workspace_bytes(B, H, Tq, Tk), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": f"decode_b{B}h{H}_tq{Tq}_tk{Tk}_{dtype}", "B": B, "H": H,
+           "Tq": Tq, "Tk": Tk, "causal": True, "scale": scale,
+           "kernels": ["decode_split16", "decode_combine16"]}
+    osa.attn_decode_stream(qd, kv[0][0], kv[0][1], o, lse, ws, True, scale, stream)
+    torch.cuda.synchronize()
+    if with_oracle:
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention_kv(q, caches[0][0], caches[0][1], True, scale,
+                                     threads=threads)
+        dt = time.perf_counter() - t0
+        eo = float(np.abs(o.float().cpu().numpy() - ro).max())
+        el = float(np.abs(lse.cpu().numpy() - rl).max())
+        ok = eo <= BF16_TOL and el <= BF16_TOL and bool(torch.isfinite(o.float()).all())
+        out["parity"] = {"rows": B * H * Tq, "max_abs_err_o": eo, "max_abs_err_lse": el,
+                         "bound": BF16_TOL, "pass": ok}
+        kv_bytes = 2 * B * H * Tk * 64 * (4 if dtype == "f32" else 2)
+        out["cpu_baseline"] = {
+            "value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"every row of the decode workload in {dt:.2f} s on {threads} "
+                      f"threads of {cpu_model()}"}
+        log(f"decode parity: {out['parity']}")
+        if not ok:
+            log("decode correctness gate FAILED: not timing it")
+            out["pass"] = False
+            return out
+    for i in range(3 * copies):
+        k, v = kv[i % copies]
+        osa.attn_decode_stream(qd, k, v, o, lse, ws, True, scale, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        k, v = kv[i % copies]
+        a.record(stream)
+        osa.attn_decode_stream(qd, k, v, o, lse, ws, True, scale, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean = statistics.fmean(ms)
+    elt = 2
+    algo = 2 * B * H * Tk * 64 * elt + 2 * B * H * Tq * 64 * elt + 4 * B * H * Tq
+    achieved = algo / (mean * 1e-3) / 1e9
+    out.update({"ms": {"mean": mean, "median": statistics.median(ms), "min": min(ms)},
+                "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_call": algo},
+                "pass": True})
+    log(f"decode: mean {mean * 1e3:.1f} us, {achieved:.0f} GB/s = "
+        f"{100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s")
+    del kv, qd, o, lse, ws
+    return out
+
+
 def contrast(osa, torch, oracle, steps=10):
     """Both paths on the fp32 single-head workloads of the page
     "attention.cu" (bytes first, then a correctness gate, then time)."""
@@ -314,6 +390,8 @@ def main():
     ap.add_argument("--no-contrast", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass leg")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode (key/value cache) leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB "
                          "(reference kernel for PMC byte counters)")
@@ -391,6 +469,11 @@ def main():
         bwd = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
                            with_oracle=not a.no_cpu_baseline)
 
+    dec = None
+    if not a.no_decode:
+        import oracle
+        dec = decode_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
+
     extra = None
     if not a.no_contrast:
         import oracle
@@ -421,6 +504,7 @@ def main():
         "parity": parity,
         "kernels": kernels,
         "backward": bwd,
+        "decode": dec,
         "contrast_fp32_single_head": extra,
         "kernel_source_sha256": kernel_source_hash(),
     }
