@@ -305,17 +305,89 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
     mean = statistics.fmean(ms)
+    # a call lasts tens of microseconds, less than the host's own time per
+    # call, so each event pair also catches any host-side stall before the
+    # launch; the median is the call's duration, the mean is reported too
+    med = statistics.median(ms)
     elt = 2
     algo = 2 * B * H * Tk * 64 * elt + 2 * B * H * Tq * 64 * elt + 4 * B * H * Tq
-    achieved = algo / (mean * 1e-3) / 1e9
+    achieved = algo / (med * 1e-3) / 1e9
     out.update({"ms": {"mean": mean, "median": statistics.median(ms), "min": min(ms)},
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                              "algorithmic_bytes_per_call": algo},
                 "pass": True})
-    log(f"decode: mean {mean * 1e3:.1f} us, {achieved:.0f} GB/s = "
+    log(f"decode: median {med * 1e3:.1f} us (mean {mean * 1e3:.1f}), {achieved:.0f} GB/s = "
         f"{100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s")
     del kv, qd, o, lse, ws
+    return out
+
+
+def head_dim_leg(osa, torch, oracle, D, B=4, H=12, T=8192, dtype="bf16", steps=10,
+                 with_oracle=True, gate_rows=512):
+    """The fused forward at another head dimension (32 or 128) on the same
+    4 x 12 x 8192 causal shape: a correctness gate against the double oracle
+    on sampled rows, then HIP-event timing. Bound by the matrix cores like
+    D = 64: 4 T^2 D flop per slice, halved by the causal mask."""
+    import numpy as np
+    from online_softmax_amd.inputs import make_qkv, sample_rows
+    dev = torch.device("cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = make_qkv(B, H, T, D, dtype, 2200 + D)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: osa.attn_fwd_stream(qd, kd, vd, o, lse, True, scale, stream)
+    run()
+    torch.cuda.synchronize()
+    out = {"workload": f"b{B}h{H}_t{T}_d{D}_{dtype}_causal", "B": B, "H": H, "T": T,
+           "D": D, "scale": scale, "kernels": [f"fused_hd16<{dtype}, causal, {D}>"]}
+    flops = osa.attn_flops(B, H, T, D, True)
+    if with_oracle:
+        rows = sample_rows(B, H, T, gate_rows, 2300 + D, boundaries=(64, 128, T // 2))
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention(q, k, v, True, scale, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        eo = float(np.abs(o.float().cpu().numpy().reshape(-1, D)[rows] - ro).max())
+        el = float(np.abs(lse.cpu().numpy().reshape(-1)[rows] - rl).max())
+        ok = eo <= BF16_TOL and el <= BF16_TOL and bool(torch.isfinite(o.float()).all())
+        out["parity"] = {"rows": int(len(rows)), "max_abs_err_o": eo, "max_abs_err_lse": el,
+                         "bound": BF16_TOL, "pass": ok}
+        row_flops = flops / (B * H * T)
+        out["cpu_baseline"] = {
+            "value": row_flops * len(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} sampled rows (mean causal row cost) in {dt:.2f} s on "
+                      f"{threads} threads of {cpu_model()}"}
+        log(f"D={D} parity: {out['parity']}")
+        if not ok:
+            log(f"D={D} correctness gate FAILED: not timing it")
+            out["pass"] = False
+            return out
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    mean = statistics.fmean(ms)
+    achieved = flops / (mean * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    out.update({"ms": {"mean": mean, "median": statistics.median(ms), "min": min(ms)},
+                "flop_per_call": flops,
+                "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                             "unit": "TFLOP/s", "frac": achieved / peak},
+                "pass": True})
+    log(f"D={D}: mean {mean:.4f} ms, {achieved:.1f} TFLOP/s = "
+        f"{100 * achieved / peak:.1f}% of {peak}")
+    del qd, kd, vd, o, lse
     return out
 
 
@@ -392,6 +464,8 @@ def main():
                     help="skip the backward-pass leg")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode (key/value cache) leg")
+    ap.add_argument("--no-head-dims", action="store_true",
+                    help="skip the head dimension 32 / 128 legs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB "
                          "(reference kernel for PMC byte counters)")
@@ -474,6 +548,12 @@ def main():
         import oracle
         dec = decode_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
 
+    hds = None
+    if not a.no_head_dims:
+        import oracle
+        hds = {str(D): head_dim_leg(osa, torch, oracle, D, with_oracle=not a.no_cpu_baseline)
+               for D in (32, 128)}
+
     extra = None
     if not a.no_contrast:
         import oracle
@@ -505,6 +585,7 @@ def main():
         "kernels": kernels,
         "backward": bwd,
         "decode": dec,
+        "head_dims": hds,
         "contrast_fp32_single_head": extra,
         "kernel_source_sha256": kernel_source_hash(),
     }

@@ -124,6 +124,33 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name: str, shape, dtype, device):
+    """Raise ValueError unless tensor t (None allowed only where the caller
+    skips the check) is contiguous, on `device`, of `dtype` and `shape`: the
+    C ABI takes bare pointers and trusts their extents."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(int(x) for x in t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _expect_lse(lse, shape, device):
+    import torch
+    if lse is not None:
+        _expect(lse, "lse", shape, torch.float32, device)
+
+
+def _expect_workspace(ws, device):
+    if ws is None or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+
+
 def _stream(stream, device):
     import torch
     if stream is None:
@@ -143,6 +170,9 @@ def attn_fwd_stream(q, k, v, o, lse, causal: bool, scale: float, stream=None):
     """Fused forward into caller-owned o ([B,H,T,D], q's dtype) and lse
     ([B,H,T] float32 or None) on `stream` (default: the current stream)."""
     B, H, T, D = _dims(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(t, name, q.shape, q.dtype, q.device)
+    _expect_lse(lse, (B, H, T), q.device)
     st = _lib().attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                 B, H, T, D, int(bool(causal)), float(scale),
                                 dtype_code(q), _stream(stream, q.device))
@@ -152,6 +182,9 @@ def attn_fwd_stream(q, k, v, o, lse, causal: bool, scale: float, stream=None):
 def attn_fwd(q, k, v, o, lse, causal: bool, scale: float):
     """Fused forward on the null stream."""
     B, H, T, D = _dims(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(t, name, q.shape, q.dtype, q.device)
+    _expect_lse(lse, (B, H, T), q.device)
     st = _lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
                          T, D, int(bool(causal)), float(scale), dtype_code(q))
     _check(st, "attn_fwd")
@@ -166,6 +199,10 @@ def attn_naive_fwd(q, k, v, o, lse, workspace, causal: bool, scale: float,
     """Materialising fp32 path; workspace is a caller-owned device tensor of
     at least attn_naive_workspace_bytes(B, H, T) bytes."""
     B, H, T, D = _dims(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(t, name, q.shape, q.dtype, q.device)
+    _expect_lse(lse, (B, H, T), q.device)
+    _expect_workspace(workspace, q.device)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib().attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                _ptr(workspace), nbytes, B, H, T, D,
@@ -184,6 +221,12 @@ def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
     workspace is a device tensor of at least attn_bwd_workspace_bytes(B, H,
     T) bytes."""
     B, H, T, D = _dims(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _expect(t, name, q.shape, q.dtype, q.device)
+    import torch
+    _expect(lse, "lse", (B, H, T), torch.float32, q.device)
+    _expect_workspace(workspace, q.device)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib().attn_bwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                 _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -202,7 +245,15 @@ def attn_decode_stream(q, k, v, o, lse, workspace, causal: bool, scale: float,
     """Decode: q [B, H, Tq, D] against the cache k, v [B, H, Tk, D] into o
     (q's shape) and lse ([B, H, Tq] float32 or None)."""
     B, H, Tq, D = _dims(q)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Tk, D]")
     Tk = int(k.shape[2])
+    _expect(q, "q", q.shape, q.dtype, q.device)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    for name, t in (("k", k), ("v", v)):
+        _expect(t, name, (B, H, Tk, D), q.dtype, q.device)
+    _expect_lse(lse, (B, H, Tq), q.device)
+    _expect_workspace(workspace, q.device)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib().attn_decode_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    _ptr(workspace), nbytes, B, H, Tq, Tk, D,

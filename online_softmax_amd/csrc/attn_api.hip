@@ -35,10 +35,15 @@ bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
     return true;
 }
 
-// Shape checks shared by both paths. Returns ATTN_OK or an error status.
-int check_shape(int B, int H, int T, int D) {
+// Head dimensions the 16-bit forward kernels are built for; every other
+// path (float32 forward, naive, backward, decode) takes 64 only.
+bool fwd16_head_dim(int D) { return D == 32 || D == attn::kHeadDim || D == 128; }
+
+// Shape checks shared by every path, for a head dimension the caller
+// accepts (`dim_ok`). Returns ATTN_OK or an error status.
+int check_shape(int B, int H, int T, int D, bool dim_ok) {
     if (B < 1 || H < 1 || T < 1 || D < 1) return ATTN_ERR_INVALID;
-    if (D != attn::kHeadDim) return ATTN_ERR_UNSUPPORTED;
+    if (!dim_ok) return ATTN_ERR_UNSUPPORTED;
     uint64_t bh, elems;
     if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || bh > (uint64_t)INT32_MAX)
         return ATTN_ERR_UNSUPPORTED;
@@ -58,9 +63,10 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
                     float* lse, int B, int H, int T, int D, int causal,
                     float scale, int dtype, void* stream) {
     if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, T, D);
-    if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D,
+                         dtype == ATTN_F32 ? D == attn::kHeadDim : fwd16_head_dim(D));
+    if (st != ATTN_OK) return st;
     if (!isfinite(scale)) return ATTN_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return ATTN_ERR_INVALID;
@@ -77,9 +83,12 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
     // exp2 multiplier: |scale| * log2(e); a negative scale negates Q instead
     const double c = fabs((double)scale) * 1.4426950408889634073599;
     if (!isfinite((float)c)) return ATTN_ERR_INVALID;
-    const hipError_t e = attn::launch_fused(
-        q, k, v, o, lse, B * H, T, causal ? 1 : 0, (float)c, scale < 0.0f,
-        dtype, (hipStream_t)stream);
+    const hipError_t e =
+        D == attn::kHeadDim
+            ? attn::launch_fused(q, k, v, o, lse, B * H, T, causal ? 1 : 0, (float)c,
+                                 scale < 0.0f, dtype, (hipStream_t)stream)
+            : attn::launch_fused_hd(q, k, v, o, lse, B * H, T, D, causal ? 1 : 0,
+                                    (float)c, scale < 0.0f, dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return ATTN_OK;
 }
@@ -106,7 +115,7 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
                     int D, int causal, float scale, int dtype, void* stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
         return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, T, D);
+    int st = check_shape(B, H, T, D, D == attn::kHeadDim);
     if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
     if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -155,7 +164,7 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
     if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID;
     if (B < 1 || H < 1 || Tq < 1 || Tk < 1 || D < 1) return ATTN_ERR_INVALID;
     if (Tq > Tk) return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, Tk, D);
+    int st = check_shape(B, H, Tk, D, D == attn::kHeadDim);
     if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
     if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -210,7 +219,7 @@ int attn_naive_fwd(const float* q, const float* k, const float* v, float* o,
                    int H, int T, int D, int causal, float scale, int dtype,
                    void* stream) {
     if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, T, D);
+    int st = check_shape(B, H, T, D, D == attn::kHeadDim);
     if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
     if (dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -246,9 +255,11 @@ int attn_fused_tile(int dtype, int* block_m, int* block_n) {
 int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
                        int causal, attn_traffic* out) {
     if (!out) return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, T, D);
-    if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    const bool dim_ok = path == ATTN_PATH_FUSED && dtype != ATTN_F32 ? fwd16_head_dim(D)
+                                                                     : D == attn::kHeadDim;
+    int st = check_shape(B, H, T, D, dim_ok);
+    if (st != ATTN_OK) return st;
     if (path != ATTN_PATH_FUSED && path != ATTN_PATH_NAIVE)
         return ATTN_ERR_INVALID;
     if (path == ATTN_PATH_NAIVE && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -307,7 +318,7 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
-           attn::kDecodeKernels;
+           attn::kDecodeKernels + attn::kHdKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -324,7 +335,11 @@ const char* attn_kernel_name(int kernel) {
         "bwd_q16<f16, causal>",      "bwd_q16<f16, full>",
         "decode_split16<bf16, causal>", "decode_split16<bf16, full>",
         "decode_combine16<bf16>",    "decode_split16<f16, causal>",
-        "decode_split16<f16, full>", "decode_combine16<f16>"};
+        "decode_split16<f16, full>", "decode_combine16<f16>",
+        "fused_hd16<bf16, causal, 32>", "fused_hd16<bf16, full, 32>",
+        "fused_hd16<f16, causal, 32>", "fused_hd16<f16, full, 32>",
+        "fused_hd16<bf16, causal, 128>", "fused_hd16<bf16, full, 128>",
+        "fused_hd16<f16, causal, 128>", "fused_hd16<f16, full, 128>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -333,11 +348,12 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     if (!out || kernel < 0 || kernel >= attn_kernel_count())
         return ATTN_ERR_INVALID;
     const int naive0 = attn::kFusedKernels, bwd0 = naive0 + attn::kNaiveKernels;
-    const int dec0 = bwd0 + attn::kBwdKernels;
+    const int dec0 = bwd0 + attn::kBwdKernels, hd0 = dec0 + attn::kDecodeKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
-                                     : attn::decode_kernel_ptr(kernel - dec0);
+                     : kernel < hd0  ? attn::decode_kernel_ptr(kernel - dec0)
+                                     : attn::hd_kernel_ptr(kernel - hd0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);

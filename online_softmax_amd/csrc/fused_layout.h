@@ -184,6 +184,62 @@ ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
     return row * kHeadDim * 2 + chunk * 16;
 }
 
+// ---- other head dimensions (16-bit forward, D = 32 or 128) -----------------
+// Tiles of 64 keys x D dims, rows of 2D bytes (C = D / 8 chunks of 16 B),
+// filled by direct loads of 1 KiB wave instructions (D / 8 per tile, D / 32
+// per wave). Swizzles, per D, keeping the row fragment reads (16 rows at one
+// chunk per quarter-wave) and the transposed reads (4 rows x 4 columns per
+// 16 lanes, 32 lanes per phase) free of bank conflicts:
+//   D = 128 (16 chunks, every row starts at bank 0): K chunk c of row r at
+//     c ^ (r & 15); V chunk c at c ^ (4 * (r & 3)) (the 4 rows of a
+//     transposed read land in distinct quarters of the row);
+//   D = 32 (4 chunks, 4 rows per 256 bytes): K chunk c at c ^ ((r >> 2) & 3);
+//     V needs none (a transposed read's 4 rows x 4 chunks are 256 whole
+//     bytes).
+template <int D>
+struct HeadDim {
+    static constexpr int kChunks = D / 8;
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kTileBytes = 64 * kRowBytes;
+    static constexpr int kInstr = kTileBytes / 1024;      // wave instructions per tile
+    static constexpr int kInstrPerWave = kInstr / kWaves;
+    static constexpr int kSteps = D / 16;                  // MFMA reduction steps of S
+    static constexpr int kOTiles = D / 32;                 // 32-dim tiles of O
+    ATTN_HD static int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 2) & 3); }
+    ATTN_HD static int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 0; }
+    ATTN_HD static int k_byte(int row, int chunk) {
+        return row * kRowBytes + ((chunk ^ swz_k(row)) << 4);
+    }
+    ATTN_HD static int v_byte(int row, int d) {
+        return row * kRowBytes + (((d >> 3) ^ swz_v(row)) << 4) + ((d & 7) << 1);
+    }
+    // direct load: instruction i of a tile (0 .. kInstr-1), lane l
+    ATTN_HD static void src(int i, int l, bool is_v, int* row, int* chunk) {
+        const int slot = i * 64 + l;
+        *row = slot / kChunks;
+        const int c = slot % kChunks;
+        *chunk = c ^ (is_v ? swz_v(*row) : swz_k(*row));
+    }
+    ATTN_HD static int global_byte(int i, int l, bool is_v) {
+        int row, chunk;
+        src(i, l, is_v, &row, &chunk);
+        return row * kRowBytes + chunk * 16;
+    }
+    // K fragment of S^T tile nt, step ks, lane (ql, h); nt adds 32 rows
+    ATTN_HD static int kfrag(int ql, int h, int nt, int ks) {
+        return k_byte(32 * nt + ql, 2 * ks + h);
+    }
+    // transposed V^T fragment read (8 bytes) of O^T tile mt, step ks, half;
+    // ks adds 16 rows and half 8 rows; mt needs a lane base
+    ATTN_HD static int vtr(int l, int mt, int ks, int half) {
+        const int j = l & 15, r = j >> 2, c = j & 3;
+        const int g = (l >> 4) & 1, h = l >> 5;
+        return v_byte(16 * ks + 8 * half + 4 * h + r, 32 * mt + 16 * g + 4 * c);
+    }
+    // Q fragment columns of lane-half h, step ks
+    ATTN_HD static int q_col(int h, int ks) { return 16 * ks + 8 * h; }
+};
+
 // ---- backward pass (16-bit) -----------------------------------------------
 // The backward kernels read some 64-row tiles both ways: row fragments
 // (16 consecutive rows at one 16-byte chunk per quarter-wave, as the K tile

@@ -39,14 +39,21 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
                          float* o_part, float* lse_part, int BH, int Tq, int Tk,
                          int causal, float c, bool negate_q, int dt, hipStream_t stream);
 
+// Fused forward for head dimensions 32 and 128 (16-bit dtypes only).
+hipError_t launch_fused_hd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int BH, int T, int D, int causal, float c, bool negate_q, int dt,
+                           hipStream_t stream);
+
 // Kernel table for attribute queries.
 constexpr int kFusedKernels = 6;
 constexpr int kNaiveKernels = 3;
 constexpr int kBwdKernels = 10;
 constexpr int kDecodeKernels = 6;
+constexpr int kHdKernels = 8;
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
 const void* decode_kernel_ptr(int index);
+const void* hd_kernel_ptr(int index);
 
 }  // namespace attn

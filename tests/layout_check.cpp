@@ -501,6 +501,83 @@ static void check_decode(int BH, int Tq, int Tk, bool causal) {
     for (int j = 0; j < kend_last; ++j) CHECK(covered[j] == 1, "decode key %d covered %d times", j, covered[j]);
 }
 
+// Other head dims: direct-load coverage, K fragment decode, strides and bank
+// conflicts, and the transposed V reads simulated with the hardware rule
+// against the P fragment's key order, for D = 32 and 128.
+template <int D>
+static void check_head_dim() {
+    using G = HeadDim<D>;
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        std::vector<int> cov(64 * G::kChunks, 0);
+        for (int i = 0; i < G::kInstr; ++i)
+            for (int l = 0; l < 64; ++l) {
+                int row, chunk;
+                G::src(i, l, is_v, &row, &chunk);
+                CHECK(row >= 0 && row < 64 && chunk >= 0 && chunk < G::kChunks, "D%d src range", D);
+                const int want = is_v ? G::v_byte(row, 8 * chunk) : G::k_byte(row, chunk);
+                CHECK(1024 * i + 16 * l == want, "D%d direct load slot", D);
+                CHECK(G::global_byte(i, l, is_v) == row * G::kRowBytes + chunk * 16, "D%d src", D);
+                cov[row * G::kChunks + chunk]++;
+            }
+        for (int x = 0; x < 64 * G::kChunks; ++x) CHECK(cov[x] == 1, "D%d chunk cover %d", D, cov[x]);
+    }
+    for (int nt = 0; nt < 2; ++nt)
+        for (int ks = 0; ks < G::kSteps; ++ks) {
+            for (int l = 0; l < 64; ++l) {
+                const int ql = l & 31, h = l >> 5;
+                const int b = G::kfrag(ql, h, nt, ks);
+                CHECK(b % 16 == 0 && b + 16 <= G::kTileBytes, "D%d kfrag range", D);
+                CHECK(b == G::kfrag(ql, h, 0, ks) + 32 * G::kRowBytes * nt, "D%d kfrag stride", D);
+                const int row = b / G::kRowBytes, slot = (b % G::kRowBytes) / 16;
+                CHECK(row == 32 * nt + ql && (slot ^ G::swz_k(row)) == 2 * ks + h, "D%d kfrag decode", D);
+            }
+            for (int grp = 0; grp < 4; ++grp) {
+                std::vector<int> used(64, 0);
+                for (int l = 16 * grp; l < 16 * grp + 16; ++l) {
+                    const int b = G::kfrag(l & 31, l >> 5, nt, ks);
+                    for (int x = 0; x < 4; ++x) used[(b / 4 + x) % 64]++;
+                }
+                for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "D%d K read bank conflict", D);
+            }
+        }
+    for (int mt = 0; mt < G::kOTiles; ++mt)
+        for (int ks = 0; ks < 4; ++ks)
+            for (int half = 0; half < 2; ++half) {
+                int addr[64];
+                for (int l = 0; l < 64; ++l) {
+                    addr[l] = G::vtr(l, mt, ks, half);
+                    CHECK(addr[l] % 8 == 0 && addr[l] + 8 <= G::kTileBytes, "D%d vtr range", D);
+                    CHECK(addr[l] == G::vtr(l, mt, 0, 0) + 16 * G::kRowBytes * ks +
+                                         8 * G::kRowBytes * half,
+                          "D%d vtr stride", D);
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int g0 = l & ~15, i = l & 15, h = l >> 5;
+                    for (int r = 0; r < 4; ++r) {
+                        const int src = g0 + 4 * r + i / 4;
+                        const int byte = addr[src] + 2 * (i % 4);
+                        const int row = byte / G::kRowBytes;
+                        const int slot = (byte % G::kRowBytes) / 16;
+                        const int dim = (slot ^ G::swz_v(row)) * 8 + (byte % 16) / 2;
+                        const int s8 = 4 * half + r;
+                        const int nt = ks >> 1, reg = (ks & 1) * 8 + s8;
+                        const int pkey = 32 * nt + acc_row(reg, h);
+                        CHECK(row == pkey && dim == 32 * mt + (l & 31),
+                              "D%d V tr lane %d slot %d: row %d dim %d", D, l, s8, row, dim);
+                    }
+                }
+                for (int half32 = 0; half32 < 2; ++half32) {
+                    std::vector<int> used(64, 0);
+                    for (int l = 32 * half32; l < 32 * half32 + 32; ++l)
+                        for (int x = 0; x < 2; ++x) used[(addr[l] / 4 + x) % 64]++;
+                    for (int x = 0; x < 64; ++x) CHECK(used[x] <= 1, "D%d V tr bank conflict", D);
+                }
+            }
+    for (int h = 0; h < 2; ++h)
+        for (int ks = 0; ks < G::kSteps; ++ks)
+            CHECK(G::q_col(h, ks) + 8 <= D && G::q_col(h, ks) == 16 * ks + 8 * h, "D%d q_col", D);
+}
+
 // The K / V rings of the 16-bit kernel: simulate one wave's issue order and
 // vmcnt waits (a wait leaving w loads in flight completes all older loads),
 // and check that each read finds its tile landed in its stage and that no
@@ -580,6 +657,8 @@ static void check_ring(int n, int n_main) {
 int main() {
     check_direct16();
     check_bwd_layout();
+    check_head_dim<32>();
+    check_head_dim<128>();
     for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})
         for (int Tq : {1, 2, 7, 31, 32, 33, 64, 100})
             for (int BH : {1, 6, 48})

@@ -59,7 +59,8 @@ def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, T=8, D=64,
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1),
     (dict(o=None), -1),
     (dict(B=0), -1), (dict(H=0), -1), (dict(T=0), -1), (dict(T=-5), -1),
-    (dict(D=0), -1), (dict(D=128), -2), (dict(D=32), -2),
+    (dict(D=0), -1), (dict(D=96), -2), (dict(D=16), -2), (dict(D=256), -2),
+    (dict(D=32, dtype=0), -2), (dict(D=128, dtype=0), -2),  # float32: D = 64 only
     (dict(dtype=3), -1), (dict(dtype=-1), -1),
     (dict(scale=math.inf), -1), (dict(scale=math.nan), -1),
     (dict(scale=3e38), -1),  # |scale| * log2(e) overflows float
@@ -84,7 +85,7 @@ def naive(lib, q=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1, H=1, T=8, D=64,
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(ws=None), -1), (dict(T=0), -1),
-    (dict(D=80), -2), (dict(dtype=1), -2), (dict(dtype=2), -2),
+    (dict(D=80), -2), (dict(D=32), -2), (dict(D=128), -2), (dict(dtype=1), -2), (dict(dtype=2), -2),
     (dict(dtype=7), -1), (dict(scale=math.nan), -1), (dict(ws=FAKE + 4), -1),
     (dict(ws_bytes=100), -1), (dict(lse=FAKE + 1), -1),
     (dict(B=70000, T=8), -2),  # grid y/z beyond 65535
@@ -102,7 +103,7 @@ def bwd(lib, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1,
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(dq=None), -1), (dict(ws=None), -1), (dict(T=0), -1), (dict(B=0), -1),
-    (dict(D=128), -2), (dict(dtype=0), -2), (dict(dtype=5), -1),
+    (dict(D=128), -2), (dict(D=32), -2), (dict(dtype=0), -2), (dict(dtype=5), -1),
     (dict(scale=math.nan), -1), (dict(scale=3e38), -1),
     (dict(q=FAKE + 8), -1), (dict(dq=FAKE + 2), -1), (dict(ws=FAKE + 4), -1),
     (dict(lse=FAKE + 2), -1), (dict(ws_bytes=16), -1),
@@ -131,7 +132,8 @@ def dec(lib, q=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1, H=1, Tq=1, Tk=8,
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(ws=None), -1), (dict(Tq=0), -1), (dict(Tk=0), -1),
-    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=128), -2), (dict(dtype=0), -2),
+    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=128), -2), (dict(D=32), -2),
+    (dict(dtype=0), -2),
     (dict(dtype=9), -1), (dict(scale=math.inf), -1), (dict(q=FAKE + 8), -1),
     (dict(ws=FAKE + 4), -1), (dict(lse=FAKE + 2), -1), (dict(ws_bytes=16), -1),
     (dict(Tk=1 << 25), -2),  # one cache slice over 4 GiB
@@ -230,11 +232,27 @@ def test_traffic_rejects_invalid(lib):
     assert lib.attn_traffic_bytes(2, 1, 1, 8, 64, 1, 1, ctypes.byref(out)) == -1
     assert lib.attn_traffic_bytes(1, 1, 1, 8, 64, 1, 1, ctypes.byref(out)) == -2
     assert lib.attn_traffic_bytes(0, 1, 1, 8, 63, 1, 1, ctypes.byref(out)) == -2
+    # head dims 32 and 128: the 16-bit fused path only
+    assert lib.attn_traffic_bytes(0, 1, 1, 8, 128, 1, 1, ctypes.byref(out)) == 0
+    assert lib.attn_traffic_bytes(0, 1, 1, 8, 32, 2, 1, ctypes.byref(out)) == 0
+    assert lib.attn_traffic_bytes(0, 1, 1, 8, 32, 0, 1, ctypes.byref(out)) == -2
+    assert lib.attn_traffic_bytes(1, 1, 1, 8, 128, 0, 1, ctypes.byref(out)) == -2
+
+
+@pytest.mark.parametrize("D", [32, 128])
+def test_traffic_other_head_dims(D):
+    """The fused ask for D = 32 / 128 counts the same 64-key tiles as D = 64,
+    with rows of 2 D bytes: everything scales with D."""
+    a = osa.attn_traffic_bytes(0, 2, 3, 1000, D, 1, True)
+    b = osa.attn_traffic_bytes(0, 2, 3, 1000, 64, 1, True)
+    lse_bytes = 2 * 3 * 1000 * 4
+    for key in ("floor", "ask"):
+        assert (a[key] - lse_bytes) * 64 == (b[key] - lse_bytes) * D
 
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 25
+    assert n == 33
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None

@@ -177,6 +177,26 @@ def test_matches_torch_sdpa_float64(T, causal):
                                rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("Dh", [32, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_other_head_dims_match_torch_sdpa_float64(Dh, causal):
+    """The same library check at head dimensions 32 and 128, with the
+    conventional scale 1/sqrt(D)."""
+    T = 300
+    q, k, v = make_qkv(2, 3, T, Dh, "f32", 1200 + Dh)
+    scale = 1.0 / math.sqrt(Dh)
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    q64, k64, v64 = (x.double() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q64, k64, v64, is_causal=causal, scale=scale)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = scale * (q64 @ k64.transpose(-1, -2).contiguous())
+    if causal:
+        s = s.masked_fill(~torch.ones(T, T, dtype=torch.bool).tril(), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(),
+                               rtol=0, atol=1e-12)
+
+
 # --- invariants -----------------------------------------------------------------
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -243,7 +243,7 @@ def test_lse_optional_and_stream(gpu_lib):
 
 
 def test_invalid_calls_raise_on_gpu(gpu_lib):
-    q = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros(1, 1, 8, 48, dtype=torch.bfloat16, device=DEV)  # no D = 48 kernel
     with pytest.raises(gpu_lib.AttnError):
         gpu_lib.attention(q, q, q, True, 0.125)
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=DEV)
