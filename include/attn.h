@@ -2,7 +2,8 @@
  * attn.h - C ABI of the MI355X (gfx950) fused attention forward library
  * (libattn.so).
  *
- * The operation is exact scaled-dot-product attention for head dimension 64,
+ * The operation is exact scaled-dot-product attention (head dimension 64 on
+ * every path; 32 and 128 also on the 16-bit fused forward),
  *
  *     O[b,h,i,:] = sum_j softmax_j( scale * q[b,h,i,:] . k[b,h,j,:] ) v[b,h,j,:]
  *
@@ -60,7 +61,8 @@ typedef enum {
                                   an unknown dtype, a non-finite scale, a
                                   workspace too small, a null output struct */
     ATTN_ERR_UNSUPPORTED = -2, /* a well-formed request this library does not
-                                  implement: D != 64, a non-fp32 naive call,
+                                  implement: a head dimension the path has
+                                  no kernel for, a non-fp32 naive call,
                                   a grid larger than one launch holds, or a
                                   16-bit slice over 4 GiB                    */
     ATTN_ERR_HIP = -3          /* the HIP runtime refused a launch or query;
@@ -76,7 +78,9 @@ typedef enum { ATTN_PATH_FUSED = 0, ATTN_PATH_NAIVE = 1 } attn_path;
  * o       : device, [B, H, T, D] of `dtype`, written (every element).
  * lse     : device, float32 [B, H, T], written; may be NULL to skip it.
  * B, H, T : batch, heads, tokens; each >= 1. Queries and keys share T.
- * D       : head dimension; must be 64.
+ * D       : head dimension: 64, or 32 or 128 for bf16 / f16 (one kernel is
+ *           built per head dimension, the way the pages' own kernels take it
+ *           as a compile-time constant); ATTN_ERR_UNSUPPORTED otherwise.
  * causal  : nonzero => key j is visible to query i iff j <= i (top-left
  *           aligned); zero => every key is visible.
  * scale   : multiplies q . k before the softmax (usually 1/sqrt(D)); any

@@ -94,6 +94,18 @@ def make_qkv(B: int, H: int, T: int, D: int, dtype: str, seed: int):
     return tuple(out)
 
 
+def make_gated(B: int, T: int, H: int, D: int, seed: int):
+    """Seeded inputs of the gated linear recurrence as float32 CPU tensors
+    [B, T, H, D]: q, k, v standard normal and the gate a logistic sigmoid of
+    a standard normal draw, so every gate lies in (0, 1) (the input structure
+    of the POPCORNBENCH transcript "Kimi-K2.6 l2 p24")."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    shape = (B, T, H, D)
+    q, k, v = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3))
+    gate = torch.sigmoid(torch.randn(shape, generator=g, dtype=torch.float32))
+    return q.contiguous(), k.contiguous(), v.contiguous(), gate.contiguous()
+
+
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.H, w.T, w.D, w.dtype, w.seed)
 

@@ -74,6 +74,10 @@ def _load():
             d.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [
                 ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
                 ctypes.c_void_p, ctypes.c_int]
+            r = lib.oracle_gated_recurrence
+            r.restype = ctypes.c_int
+            r.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
+                ctypes.c_void_p, ctypes.c_int]
             b = lib.oracle_attention_backward
             b.restype = ctypes.c_int
             b.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [
@@ -218,3 +222,22 @@ def attention_kv(q, k, v, causal: bool, scale: float, threads: int = 0):
     if rc != 0:
         raise RuntimeError("oracle_attention_kv failed (%d)" % rc)
     return o, lse
+
+
+def gated_recurrence(q, k, v, gate, threads: int = 0):
+    """The gated linear recurrence of the page "Kimi-K2.6 l2 p24"
+    (POPCORNBENCH) in double precision: per (batch, head) a D x D state S
+    from zero; at each step t, S[i, j] = gate[t, j] S[i, j] + k[t, i] v[t, j],
+    then y[t, j] = sum_i q[t, i] S[i, j]. q, k, v, gate: [B, T, H, D] float32
+    (or exactly widenable); returns y [B, T, H, D] float64."""
+    q, k, v, gate = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(gate)
+    if q.ndim != 4 or not (q.shape == k.shape == v.shape == gate.shape):
+        raise ValueError("q, k, v, gate must share one [B, T, H, D] shape")
+    B, T, H, D = q.shape
+    y = np.empty((B, T, H, D), np.float64)
+    rc = _load().oracle_gated_recurrence(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         gate.ctypes.data, B, T, H, D, y.ctypes.data,
+                                         int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_gated_recurrence failed (%d)" % rc)
+    return y

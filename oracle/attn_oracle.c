@@ -45,6 +45,16 @@
  * and dQ_i = scale * sum_j dS_ij k_j, dK_j = scale * sum_i dS_ij q_i,
  * dV_j = sum_i P_ij dO_i, every sum ascending in its index.
  *
+ * The gated linear recurrence (oracle_gated_recurrence) is the second
+ * workload of the pages, the recurrence of the page "Kimi-K2.6 l2 p24"
+ * (POPCORNBENCH), which has no softmax: per (batch, head) a D x D state S
+ * starts at zero and, for t = 0 .. T-1 in order,
+ *   S[i][j] <- gate[t][j] * S[i][j] + k[t][i] * v[t][j]     (every i, j)
+ *   y[t][j]  = sum_i q[t][i] * S[i][j]                       (i ascending)
+ * with q, k, v, gate and y laid out [B, T, H, D] as on that page. The gate
+ * scales each column j of the state; the update comes before the readout of
+ * the same step. In double, in that order, with no rearrangement.
+ *
  * Parity pins (each checked by the test suite against closed forms, library
  * routines or brute force, never against this file itself):
  *   T = 1 returns V; Q = 0 returns the (prefix) mean of V; one-hot scores
@@ -55,6 +65,10 @@
  *   scaled_dot_product_attention; T = 1 and Q = 0 closed forms; the key
  *   gradients sum to zero; dV does not depend on V; sum_i q_i.dQ_i equals
  *   sum_j k_j.dK_j; causal rows do not see later rows.
+ *   Gated recurrence: the closed-form sum over earlier steps with gate
+ *   products; gate 1 gives causal linear attention (float64 matmul); gate 0
+ *   keeps only the current step; a hand-computed scalar case; causality,
+ *   column and head independence, linearity in q and v.
  */
 #include <math.h>
 #include <stdint.h>
@@ -381,6 +395,41 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
 }
 
 /* Number of OpenMP threads a parallel region would use by default. */
+/* The gated linear recurrence above, for every (batch, head); inputs
+ * float32 [B, T, H, D], output y double [B, T, H, D]. Returns 0, or -1 for
+ * invalid sizes or an allocation failure. */
+int oracle_gated_recurrence(const float* q, const float* k, const float* v,
+                            const float* gate, int64_t B, int64_t T, int64_t H,
+                            int64_t D, double* y, int nthreads) {
+    if (B < 1 || T < 1 || H < 1 || D < 1) return -1;
+    int failed = 0;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t b = bh / H, h = bh % H;
+        double* S = (double*)calloc((size_t)(D * D), sizeof(double));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t row = ((b * T + t) * H + h) * D;
+            for (int64_t i = 0; i < D; ++i)
+                for (int64_t j = 0; j < D; ++j)
+                    S[i * D + j] = (double)gate[row + j] * S[i * D + j] +
+                                   (double)k[row + i] * (double)v[row + j];
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < D; ++i) acc += (double)q[row + i] * S[i * D + j];
+                y[row + j] = acc;
+            }
+        }
+        free(S);
+    }
+    return failed ? -1 : 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

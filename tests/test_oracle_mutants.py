@@ -72,9 +72,31 @@ DECODE_MUTANTS = [
                          "k + slice * Tq * D, v + slice * Tq * D")]),
 ]
 
+# mistakes in the gated linear recurrence
+RECURRENCE_MUTANTS = [
+    ("rec_gate_on_rows", [("S[i * D + j] = (double)gate[row + j] * S[i * D + j] +",
+                           "S[i * D + j] = (double)gate[row + i] * S[i * D + j] +")]),
+    ("rec_gate_after_add", [("S[i * D + j] = (double)gate[row + j] * S[i * D + j] +\n"
+                             "                                   (double)k[row + i] * (double)v[row + j];",
+                             "S[i * D + j] = (double)gate[row + j] * (S[i * D + j] +\n"
+                             "                                   (double)k[row + i] * (double)v[row + j]);")]),
+    ("rec_outer_transposed", [("(double)k[row + i] * (double)v[row + j];",
+                               "(double)k[row + j] * (double)v[row + i];")]),
+    ("rec_readout_wrong_index", [("acc += (double)q[row + i] * S[i * D + j];",
+                                  "acc += (double)q[row + i] * S[j * D + i];")]),
+    ("rec_readout_with_key", [("acc += (double)q[row + i] * S[i * D + j];",
+                               "acc += (double)k[row + i] * S[i * D + j];")]),
+    ("rec_state_not_reset", [("double* S = (double*)calloc((size_t)(D * D), sizeof(double));",
+                              "static double Sbuf[4096]; double* S = D * D <= 4096 ? Sbuf : "
+                              "(double*)calloc((size_t)(D * D), sizeof(double));"),
+                             ("        free(S);\n    }\n    return failed",
+                              "        if (S != Sbuf) free(S);\n    }\n    return failed")]),
+]
+
 CASES = [(n, e, "test_oracle_pins.py") for n, e in MUTANTS] + \
     [(n, e, "test_oracle_bwd_pins.py") for n, e in BACKWARD_MUTANTS] + \
-    [(n, e, "test_oracle_kv_pins.py") for n, e in DECODE_MUTANTS]
+    [(n, e, "test_oracle_kv_pins.py") for n, e in DECODE_MUTANTS] + \
+    [(n, e, "test_oracle_recurrence_pins.py") for n, e in RECURRENCE_MUTANTS]
 
 
 @pytest.mark.parametrize("name,edits,pins", CASES, ids=[c[0] for c in CASES])
