@@ -391,6 +391,99 @@ def head_dim_leg(osa, torch, oracle, D, B=4, H=12, T=8192, dtype="bf16", steps=1
     return out
 
 
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+
+
+def recurrence_leg(osa, torch, oracle, with_oracle=True, steps=20):
+    """The gated linear recurrence (attn_gated_recurrence_stream, float32)
+    at two sizes: the page's own 2 x 128 x 4 x 24 [B, T, H, D], which one
+    sequential pass per column bounds by latency (the figure is the call's
+    median time), and 8 x 4096 x 32 x 64, which has work for every SIMD and
+    is bound by vector arithmetic (5 B T H D^2 flop against the fp32 vector
+    peak). Each size passes a correctness gate against the double oracle
+    first; the page-size gate is also the CPU baseline."""
+    import numpy as np
+    from online_softmax_amd.inputs import make_gated
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {"kernels": ["gated_recurrence32"]}
+
+    def bound_ok(y, q, k, v, g):
+        want = oracle.gated_recurrence(q, k, v, g)
+        mag = oracle.gated_recurrence(q.abs(), k.abs(), v.abs(), g)
+        t = np.arange(q.shape[1], dtype=np.float64).reshape(1, -1, 1, 1)
+        bound = 2.0 * (q.shape[3] + t + 2) * 2.0 ** -24 * mag + 1e-30
+        ratio = float((np.abs(y - want) / bound).max())
+        return ratio, bool(np.isfinite(y).all()) and ratio <= 1.0
+
+    def timed(args, y, n):
+        run = lambda: osa.attn_gated_recurrence_stream(*args, y, stream)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    for label, (B, T, H, D), seed in (("page", (2, 128, 4, 24), 2401),
+                                      ("throughput", (8, 4096, 32, 64), 2402)):
+        q, k, v, g = make_gated(B, T, H, D, seed)
+        args = [x.to(dev) for x in (q, k, v, g)]
+        y = torch.empty_like(args[0])
+        osa.attn_gated_recurrence_stream(*args, y, stream)
+        torch.cuda.synchronize()
+        rec = {"B": B, "T": T, "H": H, "D": D}
+        if with_oracle:
+            yh = y.cpu().numpy()
+            if label == "page":
+                threads = oracle.max_threads()
+                t0 = time.perf_counter()
+                reps = 0
+                while reps < 20 or time.perf_counter() - t0 < 0.5:
+                    oracle.gated_recurrence(q, k, v, g, threads=threads)
+                    reps += 1
+                dt = (time.perf_counter() - t0) / reps
+                ratio, ok = bound_ok(yh, q, k, v, g)
+                rec["cpu_baseline"] = {
+                    "value": osa.attn_gated_recurrence_flops(B, T, H, D) / dt / 1e9,
+                    "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+                    "sample": f"the whole page-size call, {dt * 1e3:.3f} ms per call "
+                              f"({reps} calls) on {threads} threads of {cpu_model()}"}
+            else:
+                sl = [x[:1, :, :1].contiguous() for x in (q, k, v, g)]
+                ratio, ok = bound_ok(yh[:1, :, :1], *sl)
+            rec["parity"] = {"max_err_over_bound": ratio, "pass": ok,
+                             "checked": "every element" if label == "page" else
+                             "slice (b=0, h=0)"}
+            log(f"recurrence {label} parity: {rec['parity']}")
+            if not ok:
+                log(f"recurrence {label} correctness gate FAILED: not timing it")
+                rec["pass"] = False
+                out[label] = rec
+                continue
+        ms = timed(args, y, steps)
+        med = statistics.median(ms)
+        flops = osa.attn_gated_recurrence_flops(B, T, H, D)
+        rec["ms"] = {"mean": statistics.fmean(ms), "median": med, "min": min(ms)}
+        rec["flop_per_call"] = flops
+        achieved = flops / (med * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "latency" if label == "page" else "alu",
+                           "achieved": achieved, "peak": PEAK_FP32_VECTOR_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VECTOR_TFLOPS}
+        rec["pass"] = True
+        log(f"recurrence {label} {B}x{T}x{H}x{D}: median {med * 1e3:.1f} us, "
+            f"{achieved:.2f} TFLOP/s ({100 * achieved / PEAK_FP32_VECTOR_TFLOPS:.1f}% of "
+            f"the fp32 vector peak)")
+        out[label] = rec
+        del args, y
+    return out
+
+
 def contrast(osa, torch, oracle, steps=10):
     """Both paths on the fp32 single-head workloads of the page
     "attention.cu" (bytes first, then a correctness gate, then time)."""
@@ -466,6 +559,8 @@ def main():
                     help="skip the decode (key/value cache) leg")
     ap.add_argument("--no-head-dims", action="store_true",
                     help="skip the head dimension 32 / 128 legs")
+    ap.add_argument("--no-recurrence", action="store_true",
+                    help="skip the gated linear recurrence leg")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB "
                          "(reference kernel for PMC byte counters)")
@@ -554,6 +649,11 @@ def main():
         hds = {str(D): head_dim_leg(osa, torch, oracle, D, with_oracle=not a.no_cpu_baseline)
                for D in (32, 128)}
 
+    recur = None
+    if not a.no_recurrence:
+        import oracle
+        recur = recurrence_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
+
     extra = None
     if not a.no_contrast:
         import oracle
@@ -586,6 +686,7 @@ def main():
         "backward": bwd,
         "decode": dec,
         "head_dims": hds,
+        "gated_recurrence": recur,
         "contrast_fp32_single_head": extra,
         "kernel_source_sha256": kernel_source_hash(),
     }

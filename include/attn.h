@@ -191,6 +191,32 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
  * chosen from them); 0 for invalid sizes or on overflow. */
 size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk);
 
+/*
+ * attn_gated_recurrence_stream - the gated linear recurrence of the
+ * POPCORNBENCH transcript "Kimi-K2.6 l2 p24" (no softmax): per (batch,
+ * head) a D x D state S starts at zero and, for t = 0 .. T-1 in order,
+ *   S[i][j] <- gate[t][j] * S[i][j] + k[t][i] * v[t][j]   (every i, j)
+ *   y[t][j]  = sum_i q[t][i] * S[i][j].
+ *
+ * q, k, v, gate : device, float32 [B, T, H, D] (element (b,t,h,e) at
+ *                 ((b*T + t)*H + h)*D + e, the page's layout), read only.
+ * y             : device, float32 [B, T, H, D], written (every element).
+ * B, T, H, D    : each >= 1; D <= 64 and T * H * D * 4 < 2^31 bytes
+ *                 (ATTN_ERR_UNSUPPORTED beyond).
+ * stream        : hipStream_t or NULL.
+ * Pointers need 4-byte alignment. No workspace: the state lives in
+ * registers. Returns ATTN_OK once enqueued, or an error status with nothing
+ * enqueued.
+ */
+int attn_gated_recurrence_stream(const float* q, const float* k, const float* v,
+                                 const float* gate, float* y, int B, int T, int H, int D,
+                                 void* stream);
+
+/* Arithmetic convention for the recurrence: per step and state element a
+ * product k v, a multiply-add for the gate and a multiply-add for the
+ * readout, 5 flops, so 5 B T H D^2; 0 for sizes < 1. */
+double attn_gated_recurrence_flops(int B, int T, int H, int D);
+
 /* Arithmetic convention for the backward pass: five products to the
  * forward's two (dP, dV, dQ, dK and the recomputed scores), so 2.5 times
  * attn_flops ("Flash attention in PyTorch, then in Triton", section

@@ -1,9 +1,9 @@
-"""MI355X-native exact attention (head dim 64) on gfx950: the fused
-online-softmax forward and its backward pass.
+"""MI355X-native exact attention on gfx950: the fused online-softmax forward
+(head dims 32, 64, 128), its backward pass, decode against a key/value
+cache, and the gated linear recurrence.
 
-The fused kernels, the backward kernels and the materialising contrast path live in
-libattn.so (csrc/, C ABI in include/attn.h); this package is its thin
-binding. Nothing here computes attention: every step runs in the HIP kernels,
+The kernels and the materialising contrast path live in libattn.so (csrc/,
+C ABI in include/attn.h); this package is its thin binding. Nothing here computes attention: every step runs in the HIP kernels,
 and without the built library every call raises.
 """
 from .binding import (  # noqa: F401
@@ -15,4 +15,5 @@ from .binding import (  # noqa: F401
     attn_fwd_stream, attn_kernel_attributes, attn_kernel_count,
     attn_kernel_name, attn_last_hip_error, attn_naive_fwd,
     attn_naive_workspace_bytes, attn_status_string, attn_traffic_bytes,
-    dtype_code, load)
+    dtype_code, load, attn_gated_recurrence_stream, attn_gated_recurrence_flops,
+    gated_recurrence)

@@ -28,7 +28,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
            "attn_decode_workspace_bytes", "attn_traffic_bytes",
            "attn_flops", "attn_status_string", "attn_last_hip_error",
            "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
-           "attn_fused_tile")
+           "attn_fused_tile", "attn_gated_recurrence_stream",
+           "attn_gated_recurrence_flops")
 
 
 class AttnError(RuntimeError):
@@ -83,6 +84,9 @@ def load(path: str = LIBRARY):
         lib.attn_decode_stream.argtypes = [P] * 6 + [S, I, I, I, I, I, I, F, I, P]
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
         lib.attn_decode_workspace_bytes.restype = S
+        lib.attn_gated_recurrence_stream.argtypes = [P] * 5 + [I, I, I, I, P]
+        lib.attn_gated_recurrence_flops.argtypes = [I, I, I, I]
+        lib.attn_gated_recurrence_flops.restype = ctypes.c_double
         lib.attn_traffic_bytes.argtypes = [I, I, I, I, I, I, I,
                                            ctypes.POINTER(attn_traffic)]
         lib.attn_flops.argtypes = [I, I, I, I, I]
@@ -260,6 +264,32 @@ def attn_decode_stream(q, k, v, o, lse, workspace, causal: bool, scale: float,
                                    int(bool(causal)), float(scale), dtype_code(q),
                                    _stream(stream, q.device))
     _check(st, "attn_decode_stream")
+
+
+def attn_gated_recurrence_stream(q, k, v, gate, y, stream=None):
+    """Gated linear recurrence into caller-owned y; q, k, v, gate and y are
+    float32 [B, T, H, D] device tensors."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, D]")
+    B, T, H, D = (int(x) for x in q.shape)
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("y", y)):
+        _expect(t, name, q.shape, torch.float32, q.device)
+    st = _lib().attn_gated_recurrence_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(y),
+                                             B, T, H, D, _stream(stream, q.device))
+    _check(st, "attn_gated_recurrence_stream")
+
+
+def gated_recurrence(q, k, v, gate, stream=None):
+    """Allocate y with torch on q's device and run the gated recurrence."""
+    import torch
+    y = torch.empty_like(q)
+    attn_gated_recurrence_stream(q, k, v, gate, y, stream)
+    return y
+
+
+def attn_gated_recurrence_flops(B: int, T: int, H: int, D: int) -> float:
+    return float(_lib().attn_gated_recurrence_flops(B, T, H, D))
 
 
 def attn_bwd_flops(B: int, H: int, T: int, D: int, causal: bool) -> float:

@@ -55,6 +55,9 @@ int check_shape(int B, int H, int T, int D, bool dim_ok) {
 // stay below 2^32.
 constexpr uint64_t kMaxFusedWorkgroups = (1ull << 23) - 1;
 
+// Largest head dimension of the gated recurrence (8 state rows per lane).
+constexpr int kMaxRecurrenceDim = 64;
+
 }  // namespace
 
 extern "C" {
@@ -196,6 +199,34 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
     return ATTN_OK;
 }
 
+int attn_gated_recurrence_stream(const float* q, const float* k, const float* v,
+                                 const float* gate, float* y, int B, int T, int H, int D,
+                                 void* stream) {
+    if (!q || !k || !v || !gate || !y) return ATTN_ERR_INVALID;
+    if (B < 1 || T < 1 || H < 1 || D < 1) return ATTN_ERR_INVALID;
+    if (!aligned4(q) || !aligned4(k) || !aligned4(v) || !aligned4(gate) || !aligned4(y))
+        return ATTN_ERR_INVALID;
+    if (D > kMaxRecurrenceDim) return ATTN_ERR_UNSUPPORTED;
+    uint64_t bh, units, elems;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || !mul_ok(bh, (uint64_t)(D + 7) / 8, &units) ||
+        units > kMaxFusedWorkgroups)
+        return ATTN_ERR_UNSUPPORTED;
+    if (!mul_ok(bh * (uint64_t)D, (uint64_t)T, &elems) || elems > (uint64_t)INT64_MAX / 4)
+        return ATTN_ERR_UNSUPPORTED;
+    // one (batch, head) slice spans T steps of H * D floats, addressed with
+    // 32-bit signed byte offsets
+    if ((uint64_t)T * H * D * 4 > (uint64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const hipError_t e = attn::launch_recurrence(q, k, v, gate, y, B, T, H, D,
+                                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
+double attn_gated_recurrence_flops(int B, int T, int H, int D) {
+    if (B < 1 || T < 1 || H < 1 || D < 1) return 0.0;
+    return 5.0 * B * (double)T * H * (double)D * D;
+}
+
 double attn_bwd_flops(int B, int H, int T, int D, int causal) {
     return 2.5 * attn_flops(B, H, T, D, causal);
 }
@@ -318,7 +349,7 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
-           attn::kDecodeKernels + attn::kHdKernels;
+           attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -339,7 +370,11 @@ const char* attn_kernel_name(int kernel) {
         "fused_hd16<bf16, causal, 32>", "fused_hd16<bf16, full, 32>",
         "fused_hd16<f16, causal, 32>", "fused_hd16<f16, full, 32>",
         "fused_hd16<bf16, causal, 128>", "fused_hd16<bf16, full, 128>",
-        "fused_hd16<f16, causal, 128>", "fused_hd16<f16, full, 128>"};
+        "fused_hd16<f16, causal, 128>", "fused_hd16<f16, full, 128>",
+        "gated_recurrence32<D <= 8>",  "gated_recurrence32<D <= 16>",
+        "gated_recurrence32<D <= 24>", "gated_recurrence32<D <= 32>",
+        "gated_recurrence32<D <= 40>", "gated_recurrence32<D <= 48>",
+        "gated_recurrence32<D <= 56>", "gated_recurrence32<D <= 64>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -349,15 +384,17 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
         return ATTN_ERR_INVALID;
     const int naive0 = attn::kFusedKernels, bwd0 = naive0 + attn::kNaiveKernels;
     const int dec0 = bwd0 + attn::kBwdKernels, hd0 = dec0 + attn::kDecodeKernels;
+    const int rec0 = hd0 + attn::kHdKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
                      : kernel < hd0  ? attn::decode_kernel_ptr(kernel - dec0)
-                                     : attn::hd_kernel_ptr(kernel - hd0);
+                     : kernel < rec0 ? attn::hd_kernel_ptr(kernel - hd0)
+                                     : attn::recurrence_kernel_ptr(kernel - rec0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);
-    const int threads = attn::kThreads;
+    const int threads = kernel >= rec0 ? 64 : attn::kThreads;
     int per_cu = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
     if (e != hipSuccess) return hip_fail(e);

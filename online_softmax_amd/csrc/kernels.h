@@ -44,16 +44,22 @@ hipError_t launch_fused_hd(const void* q, const void* k, const void* v, void* o,
                            int BH, int T, int D, int causal, float c, bool negate_q, int dt,
                            hipStream_t stream);
 
+// Gated linear recurrence (float32, [B, T, H, D], D <= 64).
+hipError_t launch_recurrence(const float* q, const float* k, const float* v, const float* gate,
+                             float* y, int B, int T, int H, int D, hipStream_t stream);
+
 // Kernel table for attribute queries.
 constexpr int kFusedKernels = 6;
 constexpr int kNaiveKernels = 3;
 constexpr int kBwdKernels = 10;
 constexpr int kDecodeKernels = 6;
 constexpr int kHdKernels = 8;
+constexpr int kRecurrenceKernels = 8;
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
 const void* decode_kernel_ptr(int index);
 const void* hd_kernel_ptr(int index);
+const void* recurrence_kernel_ptr(int index);
 
 }  // namespace attn

@@ -142,6 +142,26 @@ def test_decode_rejects_invalid(lib, kw, status):
     assert dec(lib, **kw) == status
 
 
+def rec(lib, q=FAKE, y=FAKE, B=1, T=8, H=1, D=24):
+    return lib.attn_gated_recurrence_stream(q, FAKE, FAKE, FAKE, y, B, T, H, D, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(y=None), -1), (dict(B=0), -1), (dict(T=0), -1),
+    (dict(H=-1), -1), (dict(D=0), -1), (dict(D=65), -2), (dict(D=128), -2),
+    (dict(q=FAKE + 2), -1), (dict(y=FAKE + 1), -1),
+    (dict(T=1 << 20, H=64, D=64), -2),  # a slice beyond 2^31 bytes of offsets
+    (dict(B=1 << 16, H=1 << 16), -2),   # grid beyond one launch
+])
+def test_recurrence_rejects_invalid(lib, kw, status):
+    assert rec(lib, **kw) == status
+
+
+def test_recurrence_flops():
+    assert osa.attn_gated_recurrence_flops(2, 128, 4, 24) == 5 * 2 * 128 * 4 * 24 * 24
+    assert osa.attn_gated_recurrence_flops(0, 1, 1, 1) == 0.0
+
+
 def test_decode_workspace_bytes():
     for B, H, Tq, Tk in [(1, 1, 1, 1), (4, 12, 1, 8192), (2, 3, 33, 1000)]:
         n = osa.attn_decode_workspace_bytes(B, H, Tq, Tk)
@@ -252,7 +272,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 33
+    assert n == 41
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None
