@@ -26,6 +26,12 @@ import statistics
 import sys
 import time
 
+# The oracle's OpenMP threads go to sleep once a CPU leg ends instead of
+# spinning, so they do not take the host cores that launch the timed GPU
+# work (a spinning pool delayed a launch inside an event pair by tens of
+# milliseconds). Must be set before the OpenMP runtime starts.
+os.environ.setdefault("OMP_WAIT_POLICY", "PASSIVE")
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -38,7 +44,7 @@ BF16_TOL, F32_TOL_BASE = 2e-2, 1e-5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "fused_bf16_causal_b4h12_t8192_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "online_softmax_amd", "csrc", f)
-                  for f in ("fused_fwd.hip", "fused_layout.h", "gfx950.h")]
+                  for f in ("fused_fwd.hip", "fused_layout.h", "gfx950.h", "online_step.h")]
 
 
 def log(*a):
