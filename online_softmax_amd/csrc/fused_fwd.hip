@@ -17,12 +17,15 @@
 // RTX 4090):
 //  - 4 wave64s per workgroup, 32 query rows per wave, 128 per workgroup.
 //  - Q fragments live in VGPRs for the whole kernel.
-//  - K and V tiles go global -> VGPRs -> LDS with 128-bit loads, double
-//    buffered in padded LDS (one barrier per tile); the next tile's global
-//    loads are in flight while the current tile computes. V is transposed on
-//    its way into LDS so the PV product reads 16-byte fragments.
+//  - 16-bit K and V tiles go straight from HBM to LDS by direct buffer loads
+//    (buffer_load_dwordx4 ... lds) into XOR-swizzled rings of their own, K
+//    four tiles deep and issued three ahead, V three deep and one ahead;
+//    one barrier per tile. V^T fragments come from transposing LDS reads
+//    (ds_read_b64_tr_b16), so V is stored as it arrives.
 //  - S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}
-//    (fp32 inputs: v_mfma_f32_32x32x2_f32), fp32 accumulation.
+//    (fp32 inputs: v_mfma_f32_32x32x2_f32 from VGPR-staged, padded LDS
+//    tiles), fp32 accumulation; the 16-bit main loop is a three-stage
+//    software pipeline with a lazily moved softmax reference.
 //  - Row max / row sum: in-lane, then one v_permlane32_swap between halves.
 //  - Masks only on the diagonal and ragged tiles; tiles a whole wave cannot
 //    see are skipped by that wave (it still joins every barrier).
