@@ -25,12 +25,19 @@
 //    3-stage LDS ring, two tiles ahead, in the swizzle swz_b (fused_layout.h)
 //    that keeps both the row and the transposed fragment reads free of bank
 //    conflicts.
+//  - Both kernels are software-pipelined on half-tiles of 32 rows: while the
+//    vector ALU makes P and dS of one half (from the S the previous half
+//    computed), the matrix cores compute dP of that half and S of the next,
+//    then the half's gradient products run. The half-tile keeps the
+//    pipeline's state within 256 VGPRs, so two workgroups share a CU.
 //  - Masks: causal (key after query), and query rows past T in bwd_kv16 (key
 //    rows past T in bwd_q16); masked P and dS are set to 0 by selection, so
 //    no clamped or stale value can reach a sum.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fused_layout.h"
 #include "gfx950.h"
@@ -183,7 +190,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     const int n = nqt - t0;
     // loads of tile u: Q and dO (2 each per wave); lse by wave 0, delta by
     // wave 1 (one 4-byte-per-lane load each)
-    const int per_tile = 4 + (wave_u < 2 ? 1 : 0);
     auto issue = [&](int u) {
         const int q0 = (t0 + u) * kBwdBlockQ;
         const int st = u % kStages;
@@ -209,76 +215,155 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkt[ct][r] = dvt[ct][r] = 0.f;
 
+    // The pipeline runs on half-tiles of 32 queries (h = 2u + mt: rows
+    // 32mt .. 32mt + 31 of query tile u), so its state (S of two halves,
+    // dP, packed P and dS of one, their fragments) fits beside the
+    // accumulators at two workgroups per CU.
+    // Row fragments (A operands) of half mt of a Q or dO tile.
+    auto rows4 = [&](const char* tile, int mt, v4u32(&f)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) f[ks] = brow(tile, rb[ks], mt);
+    };
+    // acc = X B for 4 steps (X fragments f, B the lane's K or V row)
+    auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16<DT>(f[ks], bf[ks], acc);
+    };
+    // P and dS = P (dP - delta) of half mt of query tile u, P = exp2(s c -
+    // lse log2 e) made again, packed into the B operands of dV^T and dK^T
+    // (steps 2mt, 2mt + 1). EDGE tiles mask query rows past T and (causal)
+    // queries before the lane's key; the lane's queries are
+    // q0 + 32mt + acc_row(r, hh).
+    auto make_pds = [&](int u, int mt, const v16f32& s, const v16f32& dp, v4u32(&pf)[2],
+                        v4u32(&sf)[2], auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        const int st = u % kStages;
+        const int q0 = (t0 + u) * kBwdBlockQ;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int qi0 = 32 * mt + 8 * g + 4 * hh;  // 4 consecutive queries
+            const v4f32 l4 = *(const v4f32*)&lring[st][qi0];
+            const v4f32 e4 = *(const v4f32*)&ering[st][qi0];
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                float p = fast_exp2(fmaf(s[r], c, -l4[i] * kLog2e));
+                float d = p * (dp[r] - e4[i]);
+                if (EDGE) {
+                    const int qi = q0 + qi0 + i;
+                    const bool keep = qi < T && (!CAUSAL || my_key <= qi);
+                    p = keep ? p : 0.f;
+                    d = keep ? d : 0.f;
+                }
+                pv[i] = p;
+                dsv[i] = d;
+            }
+            // registers r = 4g..4g+3 belong to step 2mt + g/2, dwords
+            // 2(g&1), 2(g&1)+1
+            const int kl = g >> 1, w0 = 2 * (g & 1);
+            pf[kl][w0] = pack2<DT>(pv[0], pv[1]);
+            pf[kl][w0 + 1] = pack2<DT>(pv[2], pv[3]);
+            sf[kl][w0] = pack2<DT>(dsv[0], dsv[1]);
+            sf[kl][w0 + 1] = pack2<DT>(dsv[2], dsv[3]);
+        }
+    };
+
+    // Software pipeline over the half-tiles the wave sees: half h computes
+    // dP of half h and S of half h + 1 on the matrix cores while the vector
+    // ALU makes P and dS of half h (whose S the previous half produced),
+    // then dV^T += dO^T P and dK^T += Q^T dS over the half's 32 queries.
+    // Loads run two tiles ahead: at the top of tile u every load so far has
+    // landed (tile u + 1, whose first half the second half of tile u needs),
+    // and the barrier frees for tile u + 2 the stage tile u - 1 used.
+    // First tile the wave sees (causal: the block's first query tile ends
+    // before the keys of waves 2 and 3), from the wave-uniform copy of the
+    // wave index, so the loop counter and the load offsets stay scalar.
+    const int uw = bwd_kv_first_seen(kb, wave_u, n, CAUSAL);
+    auto edge_of = [&](int u) { return bwd_kv_edge(kb, wave_u, u, T, CAUSAL); };
+    using Y = std::integral_constant<bool, true>;
+    using N = std::integral_constant<bool, false>;
+    auto half = [&](int u, int mt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int st = u % kStages;
+        v4u32 fd[4], fs[4];
+        rows4(dring[st], mt, fd);
+        if (NEXT) {
+            if (mt == 0)
+                rows4(qring[st], 1, fs);
+            else
+                rows4(qring[(u + 1) % kStages], 0, fs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        v16f32 dp;
+        v4u32 pf[2], sf[2];
+        prod4(fd, vf, dp);
+        if (NEXT) prod4(fs, kf, snext);
+        make_pds(u, mt, scur, dp, pf, sf, edge_tag);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kl = 0; kl < 2; ++kl)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                dvt[ct] = mfma16<DT>(btr(dring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), pf[kl],
+                                     dvt[ct]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kl = 0; kl < 2; ++kl)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                dkt[ct] = mfma16<DT>(btr(qring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), sf[kl],
+                                     dkt[ct]);
+    };
+    auto tile = [&](int u, v16f32& sa, v16f32& sb, auto next_tag, auto edge_tag) {
+        half(u, 0, sa, sb, Y(), edge_tag);
+        half(u, 1, sb, sa, next_tag, edge_tag);
+    };
+    auto sync_issue = [&](int u) {
+        if (u > 0) {
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        if (u + 2 < n) issue(u + 2);
+    };
+
     if (n >= 1) issue(0);
     if (n >= 2) issue(1);
-    for (int u = 0; u < n; ++u) {
-        // tile u landed for this wave (tile u+1 may still be in flight)
-        if (u + 1 < n) {
-            if (per_tile == 5) wait_vmcnt<5>(); else wait_vmcnt<4>();
-        } else {
-            wait_vmcnt<0>();
+    wait_vmcnt<0>();
+    __syncthreads();
+    int u = 0;
+    for (; u < uw && u < n; ++u) sync_issue(u);  // tiles the wave does not see
+    if (u < n) {
+        v16f32 sa, sb;
+        {
+            // S of the first half of the wave's first tile (its stage
+            // landed at the last wait)
+            v4u32 f[4];
+            rows4(qring[u % kStages], 0, f);
+            prod4(f, kf, sa);
         }
-        __syncthreads();
-        if (u + 2 < n) issue(u + 2);
-        const int qt = t0 + u;
-        const int q0 = qt * kBwdBlockQ;
-        if (CAUSAL && q0 + kBwdBlockQ - 1 < kw0) continue;  // the wave's keys see none
-        const int st = u % kStages;
-        const char* qt_ = qring[st];
-        const char* dt_ = dring[st];
-        v16f32 s[2], dp[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[mt][r] = dp[mt][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                s[mt] = mfma16<DT>(brow(qt_, rb[ks], mt), kf[ks], s[mt]);
-                dp[mt] = mfma16<DT>(brow(dt_, rb[ks], mt), vf[ks], dp[mt]);
+        // Only the wave's first tile can hold the causal diagonal and only
+        // the slice's last tile can be ragged (bwd_kv_edge in
+        // fused_layout.h; the host check walks every block, wave and
+        // length), so the loop between them runs without masks; the first
+        // tile always takes the masked form.
+        sync_issue(u);
+        if (u + 1 < n) {
+            tile(u, sa, sb, Y(), Y());
+            for (++u; u + 1 < n; ++u) {
+                sync_issue(u);
+                tile(u, sa, sb, Y(), N());
             }
-        // P and dS; the lane's queries are q0 + 32mt + acc_row(r, hh)
-        v4u32 pf[4], sf[4];
-        const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + kBwdBlockQ > T;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int qi0 = 32 * mt + 8 * g + 4 * hh;  // 4 consecutive queries
-                const v4f32 l4 = *(const v4f32*)&lring[st][qi0];
-                const v4f32 e4 = *(const v4f32*)&ering[st][qi0];
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;
-                    float p = fast_exp2(fmaf(s[mt][r], c, -l4[i] * kLog2e));
-                    float d = p * (dp[mt][r] - e4[i]);
-                    if (edge) {
-                        const int qi = q0 + qi0 + i;
-                        const bool keep = qi < T && (!CAUSAL || my_key <= qi);
-                        p = keep ? p : 0.f;
-                        d = keep ? d : 0.f;
-                    }
-                    pv[i] = p;
-                    dsv[i] = d;
-                }
-                // registers r = 4g..4g+3 of half-tile mt belong to step
-                // ks = 2mt + g/2, dwords 2(g&1), 2(g&1)+1
-                const int ks = 2 * mt + (g >> 1), w0 = 2 * (g & 1);
-                pf[ks][w0] = pack2<DT>(pv[0], pv[1]);
-                pf[ks][w0 + 1] = pack2<DT>(pv[2], pv[3]);
-                sf[ks][w0] = pack2<DT>(dsv[0], dsv[1]);
-                sf[ks][w0 + 1] = pack2<DT>(dsv[2], dsv[3]);
-            }
-        // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                dvt[ct] = mfma16<DT>(btr(dt_, tb[ct][0], tb[ct][1], ks), pf[ks], dvt[ct]);
-                dkt[ct] = mfma16<DT>(btr(qt_, tb[ct][0], tb[ct][1], ks), sf[ks], dkt[ct]);
-            }
+            sync_issue(u);
+            if (edge_of(u))
+                tile(u, sa, sb, N(), Y());
+            else
+                tile(u, sa, sb, N(), N());
+        } else {
+            tile(u, sa, sb, N(), Y());
+        }
     }
     if (my_key < T) {
         store_rows<DT>(dk + base + (int64_t)my_key * kHeadDim, dkt, scale, hh);
@@ -360,63 +445,133 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[ct][r] = 0.f;
 
-    if (n >= 1) issue(0);
-    if (n >= 2) issue(1);
-    for (int u = 0; u < n; ++u) {
-        if (u + 1 < n)
-            wait_vmcnt<4>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();
-        if (u + 2 < n) issue(u + 2);
-        const int k0 = u * BN;
-        if (CAUSAL && k0 > wq0 + 31) continue;  // no key of the tile is visible
-        const int st = u % kStages;
-        const char* kt_ = kring[st];
-        const char* vt_ = vring[st];
-        v16f32 s[2], dp[2];
+    // The pipeline runs on half-tiles of 32 keys (h = 2u + nt: keys
+    // k0 + 32nt .. k0 + 32nt + 31 of key tile u), so its state (S^T of two
+    // halves, dP^T, packed dS^T of one, their fragments) fits beside the
+    // accumulators at two workgroups per CU.
+    // Row fragments (A operands) of half nt of a K or V tile.
+    auto rows4 = [&](const char* tile, int nt, v4u32(&f)[4]) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int ks = 0; ks < 4; ++ks) f[ks] = brow(tile, rb[ks], nt);
+    };
+    // acc = X B for 4 steps (X fragments f, B the lane's Q or dO row)
+    auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[nt][r] = dp[nt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16<DT>(f[ks], bf[ks], acc);
+    };
+    // dS^T = P (dP - delta) of half nt of key tile u, with P = exp2(s c -
+    // lse2) made again, packed into the B operands of dQ^T (steps 2nt,
+    // 2nt + 1). EDGE tiles mask keys past T and (causal) keys after the
+    // lane's query; the lane's keys are k0 + 32nt + acc_row(r, hh).
+    auto make_ds = [&](int u, int nt, const v16f32& s, const v16f32& dp, v4u32(&sf)[2],
+                       auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        const int k0 = u * BN + 32 * nt;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                s[nt] = mfma16<DT>(brow(kt_, rb[ks], nt), qf[ks], s[nt]);
-                dp[nt] = mfma16<DT>(brow(vt_, rb[ks], nt), of[ks], dp[nt]);
-            }
-        // dS^T; the lane's keys are k0 + 32nt + acc_row(r, hh)
-        v4u32 sf[4];
-        const bool edge = (CAUSAL && k0 + BN - 1 > wq0) || k0 + BN > T;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int nt = ks >> 1, r0 = (ks & 1) * 8;
+        for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float d2[2];
+                float d[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int r = r0 + 2 * i + e;
-                    const float p = fast_exp2(fmaf(s[nt][r], c, -lse2));
-                    float d = p * (dp[nt][r] - dl);
-                    if (edge) {
-                        const int key = k0 + 32 * nt + acc_row(r, hh);
-                        const bool keep = key < T && (!CAUSAL || key <= my_q);
-                        d = keep ? d : 0.f;
+                    const int r = 8 * kl + 2 * i + e;
+                    float p = fast_exp2(fmaf(s[r], c, -lse2));
+                    if (EDGE) {
+                        const int key = k0 + acc_row(r, hh);
+                        p = (key < T && (!CAUSAL || key <= my_q)) ? p : 0.f;
                     }
-                    d2[e] = d;
+                    d[e] = p * (dp[r] - dl);
                 }
-                sf[ks][i] = pack2<DT>(d2[0], d2[1]);
+                sf[kl][i] = pack2<DT>(d[0], d[1]);
             }
+    };
+
+    // Software pipeline over the half-tiles the wave sees: half h computes
+    // dP^T of half h and S^T of half h + 1 on the matrix cores while the
+    // vector ALU makes P and dS of half h (whose S^T the previous half
+    // produced), then dQ^T += K^T dS^T over the half's 32 keys. Loads run two
+    // tiles ahead: at the top of tile u every load so far has landed (tile
+    // u + 1, whose first half the second half of tile u needs), and the
+    // barrier frees for tile u + 2 the stage tile u - 1 used.
+    // The wave's last tile (causal: tiles past its last query are skipped),
+    // from the wave-uniform copy of the wave index, so the loop counter and
+    // the load offsets stay scalar.
+    const int wq0_u = qt * kBlockM + 32 * wave_u;
+    const int nw = CAUSAL ? min(n, (wq0_u + 31) / BN + 1) : n;
+    auto edge_of = [&](int u) {
+        const int k0 = u * BN;
+        return (CAUSAL && k0 + BN - 1 > wq0_u) || k0 + BN > T;
+    };
+    using Y = std::integral_constant<bool, true>;
+    using N = std::integral_constant<bool, false>;
+    auto half = [&](int u, int nt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int st = u % kStages;
+        v4u32 fd[4], fs[4];
+        rows4(vring[st], nt, fd);
+        if (NEXT) {
+            if (nt == 0)
+                rows4(kring[st], 1, fs);
+            else
+                rows4(kring[(u + 1) % kStages], 0, fs);
         }
-        // dQ^T += K^T dS^T
+        __builtin_amdgcn_sched_barrier(0);
+        v16f32 dp;
+        v4u32 sf[2];
+        prod4(fd, of, dp);
+        if (NEXT) prod4(fs, qf, snext);
+        make_ds(u, nt, scur, dp, sf, edge_tag);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dqt[ct] = mfma16<DT>(btr(kt_, tb[ct][0], tb[ct][1], ks), sf[ks], dqt[ct]);
+                dqt[ct] = mfma16<DT>(btr(kring[st], tb[ct][0], tb[ct][1], 2 * nt + kl), sf[kl],
+                                     dqt[ct]);
+    };
+    auto tile = [&](int u, v16f32& sa, v16f32& sb, auto next_tag, auto edge_tag) {
+        half(u, 0, sa, sb, Y(), edge_tag);
+        half(u, 1, sb, sa, next_tag, edge_tag);
+    };
+    auto sync_issue = [&](int u) {
+        if (u > 0) {
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        if (u + 2 < n) issue(u + 2);
+    };
+
+    if (n >= 1) issue(0);
+    if (n >= 2) issue(1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    int u = 0;
+    if (nw > 0) {
+        v16f32 sa, sb;
+        {
+            v4u32 f[4];
+            rows4(kring[0], 0, f);
+            prod4(f, qf, sa);  // S^T of the first half of tile 0
+        }
+        for (; u < nw; ++u) {
+            sync_issue(u);
+            const bool e = edge_of(u);
+            if (u + 1 < nw) {
+                if (e)
+                    tile(u, sa, sb, Y(), Y());
+                else
+                    tile(u, sa, sb, Y(), N());
+            } else {
+                if (e)
+                    tile(u, sa, sb, N(), Y());
+                else
+                    tile(u, sa, sb, N(), N());
+            }
+        }
     }
+    for (; u < n; ++u) sync_issue(u);  // tiles past the wave's last query
     if (my_q < T) store_rows<DT>(dq + base + (int64_t)my_q * kHeadDim, dqt, scale, hh);
 }
 

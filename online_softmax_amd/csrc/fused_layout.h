@@ -304,6 +304,24 @@ ATTN_HD void bwd_kv_tile_of(int block, int total, int nkb, bool causal, int* bh,
 ATTN_HD int bwd_first_qtile(int kb, bool causal) {
     return causal ? (kb * kBwdBlockKV) / kBwdBlockQ : 0;
 }
+// Wave w of the dK/dV kernel's key block kb (keys kb * kBwdBlockKV + 32w ..
+// + 31) and query tile u counted from bwd_first_qtile: the first u the wave
+// sees (causal: a tile whose last query comes before the wave's first key
+// is skipped), and whether tile u needs masks (a query before one of the
+// wave's keys, or rows past T).
+ATTN_HD int bwd_kv_first_seen(int kb, int w, int n, bool causal) {
+    const int kw0 = kb * kBwdBlockKV + 32 * w;
+    const int t0 = bwd_first_qtile(kb, causal);
+    int u = 0;
+    if (causal)
+        while (u < n && (t0 + u) * kBwdBlockQ + kBwdBlockQ - 1 < kw0) ++u;
+    return u;
+}
+ATTN_HD bool bwd_kv_edge(int kb, int w, int u, int T, bool causal) {
+    const int kw0 = kb * kBwdBlockKV + 32 * w;
+    const int q0 = (bwd_first_qtile(kb, causal) + u) * kBwdBlockQ;
+    return (causal && q0 < kw0 + 31) || q0 + kBwdBlockQ > T;
+}
 
 // ---- decode (few queries against a key/value cache) -------------------------
 // A workgroup takes one tile of kDecTile queries and one chunk of keys; its 4

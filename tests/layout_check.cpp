@@ -501,6 +501,32 @@ static void check_decode(int BH, int Tq, int Tk, bool causal) {
     for (int j = 0; j < kend_last; ++j) CHECK(covered[j] == 1, "decode key %d covered %d times", j, covered[j]);
 }
 
+// The pipelined dK/dV kernel masks only the wave's first tile and the last
+// tile: every tile strictly between them must need no mask.
+static void check_bwd_kv_edges() {
+    for (int causal = 0; causal < 2; ++causal)
+        for (int T = 1; T <= 1500; T += (T < 300 ? 1 : 37)) {
+            const int nkb = (T + kBwdBlockKV - 1) / kBwdBlockKV;
+            const int nqt = (T + kBwdBlockQ - 1) / kBwdBlockQ;
+            for (int kb = 0; kb < nkb; ++kb) {
+                const int n = nqt - bwd_first_qtile(kb, causal);
+                CHECK(n >= 1, "bwd kv: block with no query tile");
+                for (int w = 0; w < kWaves; ++w) {
+                    const int uw = bwd_kv_first_seen(kb, w, n, causal);
+                    for (int u = uw + 1; u + 1 < n; ++u)
+                        CHECK(!bwd_kv_edge(kb, w, u, T, causal),
+                              "bwd kv: middle tile %d of block %d wave %d T %d needs masks", u, kb,
+                              w, T);
+                    // tiles before uw hold no visible pair for the wave
+                    for (int u = 0; u < uw; ++u) {
+                        const int q_last = (bwd_first_qtile(kb, causal) + u) * kBwdBlockQ + kBwdBlockQ - 1;
+                        CHECK(q_last < kb * kBwdBlockKV + 32 * w, "bwd kv: skipped tile is visible");
+                    }
+                }
+            }
+        }
+}
+
 // Other head dims: direct-load coverage, K fragment decode, strides and bank
 // conflicts, and the transposed V reads simulated with the hardware rule
 // against the P fragment's key order, for D = 32 and 128.
@@ -657,6 +683,7 @@ static void check_ring(int n, int n_main) {
 int main() {
     check_direct16();
     check_bwd_layout();
+    check_bwd_kv_edges();
     check_head_dim<32>();
     check_head_dim<128>();
     for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})
