@@ -498,12 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
     // The wave's last tile (causal: tiles past its last query are skipped),
     // from the wave-uniform copy of the wave index, so the loop counter and
     // the load offsets stay scalar.
-    const int wq0_u = qt * kBlockM + 32 * wave_u;
-    const int nw = CAUSAL ? min(n, (wq0_u + 31) / BN + 1) : n;
-    auto edge_of = [&](int u) {
-        const int k0 = u * BN;
-        return (CAUSAL && k0 + BN - 1 > wq0_u) || k0 + BN > T;
-    };
+    const int nw = bwd_q_tiles_seen(qt, wave_u, n, CAUSAL);
     using Y = std::integral_constant<bool, true>;
     using N = std::integral_constant<bool, false>;
     auto half = [&](int u, int nt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag) {
@@ -555,21 +550,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
             rows4(kring[0], 0, f);
             prod4(f, qf, sa);  // S^T of the first half of tile 0
         }
-        for (; u < nw; ++u) {
+        // Only the wave's last tile can need masks (bwd_q_edge in
+        // fused_layout.h; the host check walks every tile, wave and
+        // length), so the loop before it runs without masks and the last
+        // tile always takes the masked form.
+        for (; u + 1 < nw; ++u) {
             sync_issue(u);
-            const bool e = edge_of(u);
-            if (u + 1 < nw) {
-                if (e)
-                    tile(u, sa, sb, Y(), Y());
-                else
-                    tile(u, sa, sb, Y(), N());
-            } else {
-                if (e)
-                    tile(u, sa, sb, N(), Y());
-                else
-                    tile(u, sa, sb, N(), N());
-            }
+            tile(u, sa, sb, Y(), N());
         }
+        sync_issue(u);
+        tile(u, sa, sb, N(), Y());
+        ++u;
     }
     for (; u < n; ++u) sync_issue(u);  // tiles past the wave's last query
     if (my_q < T) store_rows<DT>(dq + base + (int64_t)my_q * kHeadDim, dqt, scale, hh);

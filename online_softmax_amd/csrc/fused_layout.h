@@ -322,6 +322,21 @@ ATTN_HD bool bwd_kv_edge(int kb, int w, int u, int T, bool causal) {
     const int q0 = (bwd_first_qtile(kb, causal) + u) * kBwdBlockQ;
     return (causal && q0 < kw0 + 31) || q0 + kBwdBlockQ > T;
 }
+// Wave w of the dQ kernel's query tile qt (queries qt * kBlockM + 32w ..
+// + 31) and key tile u of kBlockN16 keys: how many key tiles the wave sees
+// (causal: none past its last query), and whether tile u needs masks (a key
+// after one of the wave's queries, or keys past T).
+ATTN_HD int bwd_q_tiles_seen(int qt, int w, int n, bool causal) {
+    const int wq0 = qt * kBlockM + 32 * w;
+    if (!causal) return n;
+    const int last = (wq0 + 31) / kBlockN16 + 1;
+    return last < n ? last : n;
+}
+ATTN_HD bool bwd_q_edge(int qt, int w, int u, int T, bool causal) {
+    const int wq0 = qt * kBlockM + 32 * w;
+    const int k0 = u * kBlockN16;
+    return (causal && k0 + kBlockN16 - 1 > wq0) || k0 + kBlockN16 > T;
+}
 
 // ---- decode (few queries against a key/value cache) -------------------------
 // A workgroup takes one tile of kDecTile queries and one chunk of keys; its 4

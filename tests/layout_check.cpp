@@ -527,6 +527,30 @@ static void check_bwd_kv_edges() {
         }
 }
 
+// The pipelined dQ kernel masks only the wave's last visible key tile.
+static void check_bwd_q_edges() {
+    for (int causal = 0; causal < 2; ++causal)
+        for (int T = 1; T <= 1500; T += (T < 300 ? 1 : 37)) {
+            const int nq = (T + kBlockM - 1) / kBlockM;
+            for (int qt = 0; qt < nq; ++qt) {
+                const int n = key_tiles(qt, T, kBlockN16, causal);
+                for (int w = 0; w < kWaves; ++w) {
+                    const int nw = bwd_q_tiles_seen(qt, w, n, causal);
+                    const int wq0 = qt * kBlockM + 32 * w;
+                    for (int u = 0; u + 1 < nw; ++u)
+                        CHECK(!bwd_q_edge(qt, w, u, T, causal),
+                              "bwd q: tile %d of query tile %d wave %d T %d needs masks", u, qt,
+                              w, T);
+                    // tiles past nw hold no key the wave's queries see
+                    for (int u = nw; u < n; ++u)
+                        CHECK(causal && u * kBlockN16 > wq0 + 31, "bwd q: skipped tile is visible");
+                    // every visible key tile is among the first nw
+                    if (wq0 < T) CHECK(nw >= 1, "bwd q: a wave with rows sees no tile");
+                }
+            }
+        }
+}
+
 // Other head dims: direct-load coverage, K fragment decode, strides and bank
 // conflicts, and the transposed V reads simulated with the hardware rule
 // against the P fragment's key order, for D = 32 and 128.
@@ -684,6 +708,7 @@ int main() {
     check_direct16();
     check_bwd_layout();
     check_bwd_kv_edges();
+    check_bwd_q_edges();
     check_head_dim<32>();
     check_head_dim<128>();
     for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})
