@@ -240,7 +240,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
                         v4u32(&sf)[2], auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         const int st = u % kStages;
-        const int q0 = (t0 + u) * kBwdBlockQ;
+        // query q0 + 32mt + 8g + 4hh + i is kept when it is below T and
+        // (causal) not before the lane's key: both tests against per-lane
+        // bases with the constant 32mt + 8g + i
+        const int q0h = (t0 + u) * kBwdBlockQ + 4 * hh;
+        const int room = T - q0h;         // keep while offset < room
+        const int lag = my_key - q0h;     // causal: keep while offset >= lag
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int qi0 = 32 * mt + 8 * g + 4 * hh;  // 4 consecutive queries
@@ -251,15 +256,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
                 float p = fast_exp2(fmaf(s[r], c, -l4[i] * kLog2e));
-                float d = p * (dp[r] - e4[i]);
-                if (EDGE) {
-                    const int qi = q0 + qi0 + i;
-                    const bool keep = qi < T && (!CAUSAL || my_key <= qi);
-                    p = keep ? p : 0.f;
-                    d = keep ? d : 0.f;
+                if (EDGE) {  // a masked p is 0, so its dS is too
+                    const int off = 32 * mt + 8 * g + i;
+                    p = (off < room && (!CAUSAL || off >= lag)) ? p : 0.f;
                 }
                 pv[i] = p;
-                dsv[i] = d;
+                dsv[i] = p * (dp[r] - e4[i]);
             }
             // registers r = 4g..4g+3 belong to step 2mt + g/2, dwords
             // 2(g&1), 2(g&1)+1
@@ -285,11 +287,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     auto edge_of = [&](int u) { return bwd_kv_edge(kb, wave_u, u, T, CAUSAL); };
     using Y = std::integral_constant<bool, true>;
     using N = std::integral_constant<bool, false>;
-    auto half = [&](int u, int mt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag) {
+    // SELF: the half computes its own S first (no overlap; the masked edge
+    // tiles, which need more registers, run this way)
+    auto half = [&](int u, int mt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag,
+                    auto self_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
+        constexpr bool SELF = decltype(self_tag)::value;
         const int st = u % kStages;
+        if (SELF) {
+            v4u32 f[4];
+            rows4(qring[st], mt, f);
+            prod4(f, kf, scur);
+        }
+        // the dO fragments, then (once the dP products hold them) the Q
+        // fragments of the next half: the two sets are never live together
         v4u32 fd[4], fs[4];
         rows4(dring[st], mt, fd);
+        __builtin_amdgcn_sched_barrier(0);
+        v16f32 dp;
+        v4u32 pf[2], sf[2];
+        prod4(fd, vf, dp);
         if (NEXT) {
             if (mt == 0)
                 rows4(qring[st], 1, fs);
@@ -297,9 +314,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
                 rows4(qring[(u + 1) % kStages], 0, fs);
         }
         __builtin_amdgcn_sched_barrier(0);
-        v16f32 dp;
-        v4u32 pf[2], sf[2];
-        prod4(fd, vf, dp);
         if (NEXT) prod4(fs, kf, snext);
         make_pds(u, mt, scur, dp, pf, sf, edge_tag);
         __builtin_amdgcn_sched_barrier(0);
@@ -317,9 +331,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
                 dkt[ct] = mfma16<DT>(btr(qring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), sf[kl],
                                      dkt[ct]);
     };
-    auto tile = [&](int u, v16f32& sa, v16f32& sb, auto next_tag, auto edge_tag) {
-        half(u, 0, sa, sb, Y(), edge_tag);
-        half(u, 1, sb, sa, next_tag, edge_tag);
+    // a pipelined tile (S of its first half already in sa; leaves S of the
+    // next tile's first half in sa when NEXT)
+    auto tile = [&](int u, v16f32& sa, v16f32& sb, auto next_tag) {
+        half(u, 0, sa, sb, Y(), N(), N());
+        half(u, 1, sb, sa, next_tag, N(), N());
+    };
+    // a masked tile, each half on its own
+    auto edge_tile = [&](int u, v16f32& sa) {
+        half(u, 0, sa, sa, N(), Y(), Y());
+        half(u, 1, sa, sa, N(), Y(), Y());
     };
     auto sync_issue = [&](int u) {
         if (u > 0) {
@@ -337,32 +358,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     for (; u < uw && u < n; ++u) sync_issue(u);  // tiles the wave does not see
     if (u < n) {
         v16f32 sa, sb;
-        {
-            // S of the first half of the wave's first tile (its stage
-            // landed at the last wait)
-            v4u32 f[4];
-            rows4(qring[u % kStages], 0, f);
-            prod4(f, kf, sa);
-        }
         // Only the wave's first tile can hold the causal diagonal and only
         // the slice's last tile can be ragged (bwd_kv_edge in
         // fused_layout.h; the host check walks every block, wave and
-        // length), so the loop between them runs without masks; the first
-        // tile always takes the masked form.
+        // length), so the pipelined loop between them runs without masks.
+        // The first tile always takes the masked form.
         sync_issue(u);
-        if (u + 1 < n) {
-            tile(u, sa, sb, Y(), Y());
-            for (++u; u + 1 < n; ++u) {
+        edge_tile(u, sa);
+        ++u;
+        if (u < n) {
+            // S of the first half of tile u: its stage landed at the last
+            // wait
+            {
+                v4u32 f[4];
+                rows4(qring[u % kStages], 0, f);
+                prod4(f, kf, sa);
+            }
+            for (; u + 1 < n; ++u) {
                 sync_issue(u);
-                tile(u, sa, sb, Y(), N());
+                tile(u, sa, sb, Y());
             }
             sync_issue(u);
             if (edge_of(u))
-                tile(u, sa, sb, N(), Y());
+                edge_tile(u, sa);
             else
-                tile(u, sa, sb, N(), N());
-        } else {
-            tile(u, sa, sb, N(), Y());
+                tile(u, sa, sb, N());
         }
     }
     if (my_key < T) {
