@@ -374,7 +374,11 @@ const char* attn_kernel_name(int kernel) {
         "gated_recurrence32<D <= 8>",  "gated_recurrence32<D <= 16>",
         "gated_recurrence32<D <= 24>", "gated_recurrence32<D <= 32>",
         "gated_recurrence32<D <= 40>", "gated_recurrence32<D <= 48>",
-        "gated_recurrence32<D <= 56>", "gated_recurrence32<D <= 64>"};
+        "gated_recurrence32<D <= 56>", "gated_recurrence32<D <= 64>",
+        "gated_recurrence_wave32<D <= 8>",  "gated_recurrence_wave32<D <= 16>",
+        "gated_recurrence_wave32<D <= 24>", "gated_recurrence_wave32<D <= 32>",
+        "gated_recurrence_wave32<D <= 40>", "gated_recurrence_wave32<D <= 48>",
+        "gated_recurrence_wave32<D <= 56>", "gated_recurrence_wave32<D <= 64>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -394,7 +398,11 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);
-    const int threads = kernel >= rec0 ? 64 : attn::kThreads;
+    // threads per workgroup of the kernel's launches: the recurrence's
+    // kernel i runs i + 1 waves
+    const int threads = kernel >= rec0 + 8 ? 64
+                        : kernel >= rec0   ? 64 * (kernel - rec0 + 1)
+                                           : attn::kThreads;
     int per_cu = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
     if (e != hipSuccess) return hip_fail(e);

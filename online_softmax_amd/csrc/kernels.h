@@ -54,7 +54,7 @@ constexpr int kNaiveKernels = 3;
 constexpr int kBwdKernels = 10;
 constexpr int kDecodeKernels = 6;
 constexpr int kHdKernels = 8;
-constexpr int kRecurrenceKernels = 8;
+constexpr int kRecurrenceKernels = 16;
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);

@@ -8,19 +8,18 @@
 //
 // gfx950 design (the page's kernels give each column to one CUDA thread that
 // loops over the rows):
-//  - One wave64 owns 8 columns of one (batch, head): lane = 8 * column + g,
-//    and lane g of a column keeps the rows i = g, g + 8, ... (NI = ceil(D/8)
-//    of them) of that column in registers. The state never leaves
-//    registers; the only chain carried from step to step is one FMA per
-//    state element.
+//  - One workgroup per (batch, head); one wave64 owns 8 columns: lane =
+//    8 * column + g, and lane g of a column keeps the rows i = g, g + 8, ...
+//    (NI = ceil(D/8) of them) of that column in registers. The state never
+//    leaves registers; the only chain carried from step to step is one FMA
+//    per state element.
 //  - The readout sum over i is each lane's NI products, then a sum over the
-//    column's 8 lanes by three DPP adds (quad_perm twice, row_half_mirror):
-//    no LDS, no barrier, and waves never wait for each other.
-//  - The inputs of a block of U steps are loaded into registers while the
-//    previous block computes (q, k: the lane's NI rows; v, gate: its
-//    column), so the loads' latency hides under the arithmetic.
-//  - Rows past D carry k = 0 (their state stays 0); columns past D and
-//    steps past T compute on in-bounds data and are never stored.
+//    column's 8 lanes by three DPP adds (quad_perm twice, row_half_mirror).
+//  - With many (batch, head) slices, inputs go through LDS in blocks of
+//    steps, loaded once per workgroup with coalesced loads while the
+//    previous block computes; with few, each wave prefetches its own inputs
+//    into registers (no barrier, nothing between a load and its use but the
+//    arithmetic). Details at each kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,10 +53,13 @@ __device__ inline float load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
-// One wave per (slice, 8-column block); grid = B * H * ceil(D / 8) waves.
-// The caller guarantees T * H * D * 4 < 2^31 (byte offsets are 32-bit).
+// Few (batch, head) slices (too few workgroups to fill the GPU): latency
+// decides, so each wave loads its own inputs straight into registers, a
+// block of U steps ahead, with no LDS and no barrier. One wave per (slice,
+// 8-column block); grid = B * H * ceil(D / 8) waves. The caller guarantees
+// T * H * D * 4 < 2^31 (byte offsets are 32-bit).
 template <int NI, int U>
-__global__ __launch_bounds__(64) void gated_recurrence32(
+__global__ __launch_bounds__(64) void gated_recurrence_wave32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ gate, float* __restrict__ y, int T, int H, int D, int jblocks) {
     const int lane = threadIdx.x;
@@ -143,36 +145,163 @@ __global__ __launch_bounds__(64) void gated_recurrence32(
     }
 }
 
+// Many slices (throughput): one workgroup per (batch, head), one wave per 8
+// columns (NI = ceil(D/8) waves of 64 lanes; D <= 64). The steps go in blocks of kRecSteps: a block
+// of q, k, v and the gate (every row of the slice's steps, read once,
+// coalesced, by the whole workgroup) is staged in LDS while the previous
+// block computes, so each wave reads its inputs from LDS instead of
+// fetching q and k again per wave. In LDS, q and k of a step are stored
+// with element i at 8 (i mod 8) + i / 8, so lane g's rows g, g + 8, ... are
+// 8 consecutive floats (two 16-byte reads); v and the gate keep their
+// column order. Rows and columns past D hold 0 (written once), so their
+// state stays 0; steps past T hold 0 and are never stored.
+constexpr int kRecSteps = 16;
+// from this many (batch, head) slices on, the workgroup kernel runs (every
+// CU gets at least half a workgroup); below, the per-wave kernel
+constexpr int kRecWorkgroupSlices = 128;
+constexpr int kRecSlots = 64;  // padded row of one step
+
 template <int NI>
-static const void* rec_ptr() {
-    return (const void*)gated_recurrence32<NI, (NI <= 4 ? 8 : 4)>;
+__global__ __launch_bounds__(64 * NI) void gated_recurrence32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ gate, float* __restrict__ y, int T, int H, int D) {
+    constexpr int kThreadsR = 64 * NI;
+    constexpr int kBlockElems = 4 * kRecSteps * kRecSlots;
+    // elements a block loads: 4 tensors x kRecSteps steps x D <= 8 NI
+    constexpr int kPerThread = (4 * kRecSteps * 8 * NI + kThreadsR - 1) / kThreadsR;
+    __shared__ __attribute__((aligned(16))) float lds[2][4][kRecSteps][kRecSlots];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = lane & 7;
+    const int j = (tid >> 6) * 8 + (lane >> 3);  // this lane's column
+    const bool col_ok = j < D;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H;
+    // element (b, t, h, e) sits at ((b * T + t) * H + h) * D + e
+    const int64_t step_stride = (int64_t)H * D;
+    const int64_t base = ((int64_t)b * T * H + h) * D;
+    const float* src[4] = {q + base, k + base, v + base, gate + base};
+
+    // zero both stages once: the slots past D are never written again
+    for (int e = tid; e < 2 * kBlockElems; e += kThreadsR) (&lds[0][0][0][0])[e] = 0.f;
+
+    // thread tid carries elements tid + n * kThreadsR of a block: tensor x,
+    // step u, element i (< D only); loaded into registers, then written to
+    // their LDS slots
+    const int per_block = 4 * kRecSteps * D;
+    float buf[kPerThread];
+    auto load = [&](int blk) {
+#pragma unroll
+        for (int n = 0; n < kPerThread; ++n) {
+            const int e = tid + n * kThreadsR;
+            float val = 0.f;
+            if (e < per_block) {
+                const int x = e / (kRecSteps * D);
+                const int rem = e - x * (kRecSteps * D);
+                const int u = rem / D;
+                const int t = blk * kRecSteps + u;
+                if (t < T) val = src[x][(int64_t)t * step_stride + (rem - u * D)];
+            }
+            buf[n] = val;
+        }
+    };
+    auto stage = [&](int slot) {
+#pragma unroll
+        for (int n = 0; n < kPerThread; ++n) {
+            const int e = tid + n * kThreadsR;
+            if (e < per_block) {
+                const int x = e / (kRecSteps * D);
+                const int rem = e - x * (kRecSteps * D);
+                const int u = rem / D;
+                const int i = rem - u * D;
+                const int pos = x < 2 ? 8 * (i & 7) + (i >> 3) : i;
+                lds[slot][x][u][pos] = buf[n];
+            }
+        }
+    };
+
+    float S[NI];
+#pragma unroll
+    for (int r = 0; r < NI; ++r) S[r] = 0.f;
+    auto compute = [&](int slot, int t0) {
+#pragma unroll 4
+        for (int u = 0; u < kRecSteps; ++u) {
+            const float4* qrow = (const float4*)&lds[slot][0][u][8 * g];
+            const float4* krow = (const float4*)&lds[slot][1][u][8 * g];
+            const float4 q0 = qrow[0], q1 = qrow[1], k0 = krow[0], k1 = krow[1];
+            const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float vj = lds[slot][2][u][j];
+            const float gj = lds[slot][3][u][j];
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < NI; ++r) {
+                S[r] = fmaf(gj, S[r], kv[r] * vj);
+                acc = fmaf(qv[r], S[r], acc);
+            }
+            acc = sum8(acc);
+            const int t = t0 + u;
+            if (g == (u & 7) && col_ok && t < T) y[base + (int64_t)t * step_stride + j] = acc;
+        }
+    };
+
+    const int nblk = (T + kRecSteps - 1) / kRecSteps;
+    __syncthreads();  // the zeroing is done before any stage writes
+    load(0);
+    stage(0);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const bool more = blk + 1 < nblk;
+        if (more) load(blk + 1);  // in flight while this block computes
+        compute(blk & 1, blk * kRecSteps);
+        if (more) stage((blk + 1) & 1);  // that stage was last read a block ago
+        __syncthreads();
+    }
 }
 
+template <int NI>
+static const void* rec_ptr(bool per_wave) {
+    return per_wave ? (const void*)gated_recurrence_wave32<NI, (NI <= 4 ? 8 : 4)>
+                    : (const void*)gated_recurrence32<NI>;
+}
+
+// Table: entries 0 .. 7 the workgroup kernel for NI = 1 .. 8, entries
+// 8 .. 15 the per-wave kernel.
 const void* recurrence_kernel_ptr(int index) {
-    switch (index) {
-        case 0: return rec_ptr<1>();
-        case 1: return rec_ptr<2>();
-        case 2: return rec_ptr<3>();
-        case 3: return rec_ptr<4>();
-        case 4: return rec_ptr<5>();
-        case 5: return rec_ptr<6>();
-        case 6: return rec_ptr<7>();
-        case 7: return rec_ptr<8>();
+    if (index < 0 || index >= 16) return nullptr;
+    const bool w = index >= 8;
+    switch (index & 7) {
+        case 0: return rec_ptr<1>(w);
+        case 1: return rec_ptr<2>(w);
+        case 2: return rec_ptr<3>(w);
+        case 3: return rec_ptr<4>(w);
+        case 4: return rec_ptr<5>(w);
+        case 5: return rec_ptr<6>(w);
+        case 6: return rec_ptr<7>(w);
+        case 7: return rec_ptr<8>(w);
         default: return nullptr;
     }
 }
 
 hipError_t launch_recurrence(const float* q, const float* k, const float* v, const float* gate,
                              float* y, int B, int T, int H, int D, hipStream_t stream) {
-    const int ni = (D + 7) / 8;
+    const int ni = (D + 7) / 8;  // 8 columns per wave
+    if ((int64_t)B * H < kRecWorkgroupSlices) {
+        const void* fn = recurrence_kernel_ptr(8 + ni - 1);
+        if (fn == nullptr) return hipErrorInvalidValue;
+        int jblocks = ni;
+        const dim3 grid((unsigned)((int64_t)B * H * jblocks));
+        void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&gate, (void*)&y,
+                        (void*)&T, (void*)&H, (void*)&D, (void*)&jblocks};
+        return hipLaunchKernel(fn, grid, dim3(64), args, 0, stream);
+    }
     const void* fn = recurrence_kernel_ptr(ni - 1);
     if (fn == nullptr) return hipErrorInvalidValue;
-    int jblocks = ni;  // 8 columns per wave
-    const dim3 grid((unsigned)((int64_t)B * H * jblocks));
-    const dim3 block(64);
+    const dim3 grid((unsigned)((int64_t)B * H));
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&gate, (void*)&y,
-                    (void*)&T, (void*)&H, (void*)&D, (void*)&jblocks};
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+                    (void*)&T, (void*)&H, (void*)&D};
+    return hipLaunchKernel(fn, grid, dim3(64 * ni), args, 0, stream);
 }
 
 }  // namespace attn

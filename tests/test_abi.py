@@ -272,7 +272,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 41
+    assert n == 49
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None

@@ -87,3 +87,24 @@ def test_backward_metric_workload_slices(gpu_lib):
     want = oracle.attention_backward(q, k, v, dout, True, 0.125, slices=sl)
     got_sl = [g.reshape(48, 8192, 64)[sl] for g in got]
     check_grads("4x12x8192 slices 0,47", got_sl, want)
+
+
+@pytest.mark.parametrize("T", [77, 300])
+def test_bf16_gradients_within_twice_torch_cpu_error(gpu_lib, T):
+    """The backward's own rule on its page ("Flash attention in PyTorch, then
+    in Triton", section "Backwards, and training with it"): for each of dQ,
+    dK and dV, our bf16 error against float64 is at most twice that of
+    torch's own attention in bf16 (here torch's CPU kernel and its autograd),
+    plus a tiny margin."""
+    q, k, v, dout = case(2, 3, T, "bf16", 4200 + T)
+    got = gpu_backward(gpu_lib, q, k, v, dout, True, 0.125)
+    want = oracle.attention_backward(q, k, v, dout, True, 0.125)
+    tq, tk, tv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                           scale=0.125)
+    theirs = [g.float().numpy() for g in torch.autograd.grad(out, (tq, tk, tv), dout)]
+    for name, g, t, w in zip(("dQ", "dK", "dV"), got, theirs, want):
+        ours_err = float(np.abs(np.asarray(g, np.float64).reshape(w.shape) - w).max())
+        their_err = float(np.abs(t.astype(np.float64) - w).max())
+        flush_print(f"    bf16 T={T} {name}: ours {ours_err:.3e} torch-cpu {their_err:.3e}")
+        assert ours_err <= 2 * their_err + 1e-5, name

@@ -59,11 +59,23 @@ def test_page_size(gpu_lib):
 @pytest.mark.parametrize("D", [1, 7, 8, 9, 16, 24, 33, 40, 57, 64])
 @pytest.mark.parametrize("T", [1, 5, 17, 300])
 def test_dims_and_lengths(gpu_lib, D, T):
-    """Every register-block size (ceil(D / 8) rows per lane, 1..8), head
-    dims that leave lanes idle, and lengths that end mid-block."""
+    """Few slices (the per-wave kernel): every register-block size
+    (ceil(D / 8) rows per lane, 1..8), head dims that leave lanes idle, and
+    lengths that end mid-block."""
     q, k, v, g = make_gated(2, T, 3, D, seed=7100 + 100 * D + T)
     flush_print(f"[gpu] recurrence D={D} T={T}")
     check(f"D={D} T={T}", run(gpu_lib, q, k, v, g), q, k, v, g)
+
+
+@pytest.mark.parametrize("D", [1, 7, 9, 24, 33, 57, 64])
+@pytest.mark.parametrize("T", [1, 17, 300])
+def test_many_slices(gpu_lib, D, T):
+    """128 (batch, head) slices: the workgroup kernel (inputs staged through
+    LDS in blocks of steps), every register-row count, lengths that end
+    mid-block; every element checked."""
+    q, k, v, g = make_gated(2, T, 64, D, seed=7400 + 100 * D + T)
+    flush_print(f"[gpu] recurrence 2x{T}x64x{D}")
+    check(f"2x{T}x64x{D}", run(gpu_lib, q, k, v, g), q, k, v, g)
 
 
 def test_unit_and_zero_gates(gpu_lib):
