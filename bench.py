@@ -209,35 +209,44 @@ def time_fused(osa, torch, q, k, v, o, lse, w, steps, warmup):
 
 
 def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
-                 warmup=3, with_oracle=True):
-    """The backward pass (attn_bwd_stream) on the same workload for a seeded
-    output gradient: a correctness gate against the double oracle on one
-    whole slice (also the backward's CPU baseline), then HIP-event timing.
-    Throughput uses the pages' count for the pass, five products to the
-    forward's two ("Flash attention in PyTorch, then in Triton", section
-    "Backwards, and training with it"); the two-kernel split performs seven."""
+                 warmup=3, with_oracle=True, atomic=False, cache=None):
+    """The backward pass (attn_bwd_stream, or with atomic=True
+    attn_bwd_atomic_stream) on the same workload for a seeded output
+    gradient: a correctness gate against the double oracle on one whole
+    slice (also the backward's CPU baseline; `cache` keeps the oracle's
+    gradients for the second leg), then HIP-event timing. Throughput uses
+    the pages' count for the pass, five products to the forward's two
+    ("Flash attention in PyTorch, then in Triton", section "Backwards, and
+    training with it"); the two-kernel split performs seven, the atomic
+    path five."""
     import numpy as np
     from online_softmax_amd.inputs import make_qkv
     dev = qd.device
     (dout,) = make_qkv(w.B, w.H, w.T, w.D, w.dtype, w.seed + 7)[:1]
     dd = dout.to(dev)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    ws = torch.empty(osa.attn_bwd_workspace_bytes(w.B, w.H, w.T), dtype=torch.uint8,
-                     device=dev)
+    need = (osa.attn_bwd_atomic_workspace_bytes if atomic else osa.attn_bwd_workspace_bytes)
+    ws = torch.empty(need(w.B, w.H, w.T), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    run = lambda: osa.attn_bwd_stream(qd, kd, vd, o, dd, lse, dq, dk, dv, ws,
-                                      w.causal, w.scale, stream)
+    entry = osa.attn_bwd_atomic_stream if atomic else osa.attn_bwd_stream
+    run = lambda: entry(qd, kd, vd, o, dd, lse, dq, dk, dv, ws, w.causal, w.scale, stream)
     run()
     torch.cuda.synchronize()
-    out = {"kernels": ["bwd_delta16", "bwd_kv16", "bwd_q16"]}
+    out = {"entry": "attn_bwd_atomic_stream" if atomic else "attn_bwd_stream",
+           "kernels": (["bwd_prep16", "bwd_kvq16", "bwd_dq_finish16"] if atomic
+                       else ["bwd_delta16", "bwd_kv16", "bwd_q16"])}
     flops = osa.attn_bwd_flops(w.B, w.H, w.T, w.D, w.causal)
+    performed = 5.0 if atomic else 7.0
     if with_oracle:
         sl = np.array([0])
         threads = oracle.max_threads()
+        cache = {} if cache is None else cache
         t0 = time.perf_counter()
-        want = oracle.attention_backward(q, k, v, dout, w.causal, w.scale, slices=sl,
-                                         threads=threads)
-        dt = time.perf_counter() - t0
+        if "want" not in cache:
+            cache["want"] = oracle.attention_backward(q, k, v, dout, w.causal, w.scale,
+                                                      slices=sl, threads=threads)
+            cache["dt"] = time.perf_counter() - t0
+        want, dt = cache["want"], cache["dt"]
         errs, ok = {}, True
         for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
             got = g.float().cpu().numpy().reshape(w.B * w.H, w.T, w.D)[sl]
@@ -254,7 +263,7 @@ def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
             "sample": (f"gradients of slice 0 (of {w.B * w.H}) of {w.name}, "
                        f"{slice_flops:.3e} flop by the pages' count in {dt:.2f} s "
                        f"on {threads} threads of {cpu_model()}")}
-        log(f"backward parity on slice 0: {errs}")
+        log(f"backward ({out['entry']}) parity on slice 0: {errs}")
         if not ok:
             log("backward correctness gate FAILED: not timing it")
             out["pass"] = False
@@ -265,13 +274,14 @@ def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
     peak = PEAK_TFLOPS[w.dtype]
     out.update({
         "ms": ms,
-        "flop_convention": flops, "flop_performed": flops * 7.0 / 5.0,
+        "flop_convention": flops, "flop_performed": flops * performed / 5.0,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "achieved_performed": achieved * 7.0 / 5.0},
+                     "achieved_performed": achieved * performed / 5.0},
         "pass": True})
-    log(f"backward: mean {mean:.4f} ms, {achieved:.1f} TFLOP/s by the pages' count "
-        f"({achieved * 1.4:.1f} performed) = {100 * achieved / peak:.1f}% of {peak}")
+    log(f"backward ({out['entry']}): mean {mean:.4f} ms, {achieved:.1f} TFLOP/s by the "
+        f"pages' count ({achieved * performed / 5.0:.1f} performed) = "
+        f"{100 * achieved / peak:.1f}% of {peak}")
     del dq, dk, dv, ws, dd
     return out
 
@@ -644,11 +654,16 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {a.copy_mib} MiB x 3 (PMC reference)")
 
-    bwd = None
+    bwd = bwd_atomic = None
     if not a.no_backward and w.dtype != "f32":
         import oracle
+        cache = {}
         bwd = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
-                           with_oracle=not a.no_cpu_baseline)
+                           with_oracle=not a.no_cpu_baseline, cache=cache)
+        bwd_atomic = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
+                                  with_oracle=not a.no_cpu_baseline, atomic=True,
+                                  cache=cache)
+        bwd_atomic.pop("cpu_baseline", None)
 
     dec = None
     if not a.no_decode:
@@ -696,6 +711,7 @@ def main():
         "parity": parity,
         "kernels": kernels,
         "backward": bwd,
+        "backward_atomic": bwd_atomic,
         "decode": dec,
         "head_dims": hds,
         "gated_recurrence": recur,

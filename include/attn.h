@@ -158,6 +158,35 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
 size_t attn_bwd_workspace_bytes(int B, int H, int T);
 
 /*
+ * attn_bwd_atomic_stream - the same gradients as attn_bwd_stream (same
+ * arguments, same definition: "Flash attention in PyTorch, then in Triton",
+ * section "Backwards, and training with it"), computed with one main kernel
+ * per key block that makes S, P, dP and dS once and adds each block's share
+ * of dQ = scale dS K into a float32 copy of dQ with atomic adds; a last
+ * kernel rounds that copy into dq.
+ *
+ * workspace : caller-owned device buffer of at least
+ *             attn_bwd_atomic_workspace_bytes(B, H, T) bytes (16-byte
+ *             aligned): delta (float32 [B, H, T], padded to 256 bytes), then
+ *             the float32 dQ copy ([B, H, T, D]); zeroed by the call itself,
+ *             contents undefined after.
+ * dk, dv    : summed in one fixed order per element, as attn_bwd_stream.
+ * dq        : float32 sums in an order the atomics decide, so two calls may
+ *             differ in the last bits (within the same error bound).
+ *
+ * Returns and errors as attn_bwd_stream. Extra device memory: the caller's
+ * workspace only.
+ */
+int attn_bwd_atomic_stream(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int T,
+                           int D, int causal, float scale, int dtype, void* stream);
+
+/* Workspace bytes attn_bwd_atomic_stream needs: attn_bwd_workspace_bytes(B,
+ * H, T) + B*H*T*64*4; 0 for sizes < 1 or when the count overflows 64 bits. */
+size_t attn_bwd_atomic_workspace_bytes(int B, int H, int T);
+
+/*
  * attn_decode_stream - attention of Tq new queries against a key/value cache
  * of Tk tokens (decode). Query i is the token at position Tk - Tq + i, so
  * with causal != 0 it sees keys 0 .. Tk - Tq + i (the mask aligned to the

@@ -24,7 +24,8 @@ ATTN_PATH_FUSED, ATTN_PATH_NAIVE = 0, 1
 # every symbol include/attn.h declares
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
            "attn_naive_workspace_bytes", "attn_bwd_stream",
-           "attn_bwd_workspace_bytes", "attn_bwd_flops", "attn_decode_stream",
+           "attn_bwd_workspace_bytes", "attn_bwd_atomic_stream",
+           "attn_bwd_atomic_workspace_bytes", "attn_bwd_flops", "attn_decode_stream",
            "attn_decode_workspace_bytes", "attn_traffic_bytes",
            "attn_flops", "attn_status_string", "attn_last_hip_error",
            "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
@@ -79,6 +80,9 @@ def load(path: str = LIBRARY):
         lib.attn_bwd_stream.argtypes = [P] * 10 + [S, I, I, I, I, I, F, I, P]
         lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
         lib.attn_bwd_workspace_bytes.restype = S
+        lib.attn_bwd_atomic_stream.argtypes = [P] * 10 + [S, I, I, I, I, I, F, I, P]
+        lib.attn_bwd_atomic_workspace_bytes.argtypes = [I, I, I]
+        lib.attn_bwd_atomic_workspace_bytes.restype = S
         lib.attn_bwd_flops.argtypes = [I, I, I, I, I]
         lib.attn_bwd_flops.restype = ctypes.c_double
         lib.attn_decode_stream.argtypes = [P] * 6 + [S, I, I, I, I, I, I, F, I, P]
@@ -219,11 +223,8 @@ def attn_bwd_workspace_bytes(B: int, H: int, T: int) -> int:
     return int(_lib().attn_bwd_workspace_bytes(B, H, T))
 
 
-def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
-                    scale: float, stream=None):
-    """Backward pass into caller-owned dq, dk, dv (q's shape and dtype);
-    workspace is a device tensor of at least attn_bwd_workspace_bytes(B, H,
-    T) bytes."""
+def _bwd_call(entry: str, q, k, v, o, dout, lse, dq, dk, dv, workspace, causal,
+              scale, stream):
     B, H, T, D = _dims(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
                     ("dk", dk), ("dv", dv)):
@@ -232,12 +233,34 @@ def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
     _expect(lse, "lse", (B, H, T), torch.float32, q.device)
     _expect_workspace(workspace, q.device)
     nbytes = workspace.numel() * workspace.element_size()
-    st = _lib().attn_bwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+    st = getattr(_lib(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                 _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                 _ptr(workspace), nbytes, B, H, T, D,
                                 int(bool(causal)), float(scale), dtype_code(q),
                                 _stream(stream, q.device))
-    _check(st, "attn_bwd_stream")
+    _check(st, entry)
+
+
+def attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool,
+                    scale: float, stream=None):
+    """Backward pass into caller-owned dq, dk, dv (q's shape and dtype);
+    workspace is a device tensor of at least attn_bwd_workspace_bytes(B, H,
+    T) bytes."""
+    _bwd_call("attn_bwd_stream", q, k, v, o, dout, lse, dq, dk, dv, workspace,
+              causal, scale, stream)
+
+
+def attn_bwd_atomic_workspace_bytes(B: int, H: int, T: int) -> int:
+    return int(_lib().attn_bwd_atomic_workspace_bytes(B, H, T))
+
+
+def attn_bwd_atomic_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                           causal: bool, scale: float, stream=None):
+    """The backward pass with dQ summed by float32 atomics (one main kernel);
+    workspace is a device tensor of at least
+    attn_bwd_atomic_workspace_bytes(B, H, T) bytes."""
+    _bwd_call("attn_bwd_atomic_stream", q, k, v, o, dout, lse, dq, dk, dv,
+              workspace, causal, scale, stream)
 
 
 def attn_decode_workspace_bytes(B: int, H: int, Tq: int, Tk: int) -> int:
@@ -356,18 +379,21 @@ def attention(q, k, v, causal: bool = True, scale: float | None = None,
 
 
 def attention_backward(q, k, v, o, lse, dout, causal: bool = True,
-                       scale: float | None = None, stream=None):
+                       scale: float | None = None, stream=None,
+                       atomic: bool = False):
     """Allocate dq, dk, dv and the workspace with torch on q's device and run
     the backward pass for the forward (o, lse) of the same q, k, v, causal and
-    scale. Returns (dq, dk, dv)."""
+    scale: the two-kernel split, or with atomic=True the single main kernel
+    that sums dQ with atomics. Returns (dq, dk, dv)."""
     import torch
     B, H, T, D = _dims(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(attn_bwd_workspace_bytes(B, H, T), dtype=torch.uint8,
-                     device=q.device)
-    attn_bwd_stream(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
+    need = (attn_bwd_atomic_workspace_bytes if atomic else attn_bwd_workspace_bytes)(B, H, T)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    run = attn_bwd_atomic_stream if atomic else attn_bwd_stream
+    run(q, k, v, o, dout, lse, dq, dk, dv, ws, causal, scale, stream)
     return dq, dk, dv
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "fused_fwd.hip", "naive_fwd.hip", "attn_bwd.hip",
-           "attn_decode.hip", "fused_hd.hip",
+           "attn_bwd_atomic.hip", "attn_decode.hip", "fused_hd.hip",
            "recurrence.hip"]
 ARCH = "gfx950"
 

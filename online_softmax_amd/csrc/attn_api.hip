@@ -147,6 +147,55 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
     return ATTN_OK;
 }
 
+size_t attn_bwd_atomic_workspace_bytes(int B, int H, int T) {
+    const size_t rows = attn_bwd_workspace_bytes(B, H, T);
+    if (rows == 0) return 0;
+    uint64_t bh, elems, bytes;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh)) return 0;
+    if (!mul_ok(bh * (uint64_t)T, (uint64_t)attn::kHeadDim, &elems)) return 0;
+    if (!mul_ok(elems, 4, &bytes)) return 0;
+    if (bytes > UINT64_MAX - rows) return 0;
+    return (size_t)(rows + bytes);
+}
+
+int attn_bwd_atomic_stream(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int T,
+                           int D, int causal, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+        return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, T, D, D == attn::kHeadDim);
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    const void* p16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* p : p16)
+        if (!aligned16(p)) return ATTN_ERR_INVALID;
+    if (!aligned4(lse)) return ATTN_ERR_INVALID;
+    const size_t need = attn_bwd_atomic_workspace_bytes(B, H, T);
+    if (need == 0) return ATTN_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return ATTN_ERR_INVALID;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t nkb = ((uint64_t)T + attn::kBwdBlockKV - 1) / attn::kBwdBlockKV;
+    // grids: key blocks; 32 rows per workgroup (prep); 2048 values per
+    // workgroup (finish)
+    if (nkb * bh > kMaxFusedWorkgroups || (bh * T + 31) / 32 > (uint64_t)INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
+    if ((uint64_t)T * D * 2 > UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    const double c = fabs((double)scale) * 1.4426950408889634073599;
+    if (!isfinite((float)c)) return ATTN_ERR_INVALID;
+    const size_t delta_bytes = attn_bwd_workspace_bytes(B, H, T);
+    float* delta = (float*)workspace;
+    float* dq_acc = (float*)((char*)workspace + delta_bytes);
+    const hipError_t e = attn::launch_bwd_atomic(q, k, v, o, dout, lse, dq, dk, dv, delta,
+                                                 dq_acc, B * H, T, causal ? 1 : 0, (float)c,
+                                                 scale, scale < 0.0f, dtype,
+                                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk) {
     if (B < 1 || H < 1 || Tq < 1 || Tk < Tq) return 0;
     uint64_t bh, rows;
@@ -349,7 +398,8 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
-           attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels;
+           attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels +
+           attn::kBwdAtomicKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -378,7 +428,11 @@ const char* attn_kernel_name(int kernel) {
         "gated_recurrence_wave32<D <= 8>",  "gated_recurrence_wave32<D <= 16>",
         "gated_recurrence_wave32<D <= 24>", "gated_recurrence_wave32<D <= 32>",
         "gated_recurrence_wave32<D <= 40>", "gated_recurrence_wave32<D <= 48>",
-        "gated_recurrence_wave32<D <= 56>", "gated_recurrence_wave32<D <= 64>"};
+        "gated_recurrence_wave32<D <= 56>", "gated_recurrence_wave32<D <= 64>",
+        "bwd_prep16<bf16>",          "bwd_kvq16<bf16, causal>",
+        "bwd_kvq16<bf16, full>",     "bwd_dq_finish16<bf16>",
+        "bwd_prep16<f16>",           "bwd_kvq16<f16, causal>",
+        "bwd_kvq16<f16, full>",      "bwd_dq_finish16<f16>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -389,18 +443,21 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     const int naive0 = attn::kFusedKernels, bwd0 = naive0 + attn::kNaiveKernels;
     const int dec0 = bwd0 + attn::kBwdKernels, hd0 = dec0 + attn::kDecodeKernels;
     const int rec0 = hd0 + attn::kHdKernels;
+    const int bat0 = rec0 + attn::kRecurrenceKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
                      : kernel < hd0  ? attn::decode_kernel_ptr(kernel - dec0)
                      : kernel < rec0 ? attn::hd_kernel_ptr(kernel - hd0)
-                                     : attn::recurrence_kernel_ptr(kernel - rec0);
+                     : kernel < bat0 ? attn::recurrence_kernel_ptr(kernel - rec0)
+                                     : attn::bwd_atomic_kernel_ptr(kernel - bat0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);
     // threads per workgroup of the kernel's launches: the recurrence's
     // kernel i runs i + 1 waves
-    const int threads = kernel >= rec0 + 8 ? 64
+    const int threads = kernel >= bat0     ? attn::kThreads
+                        : kernel >= rec0 + 8 ? 64
                         : kernel >= rec0   ? 64 * (kernel - rec0 + 1)
                                            : attn::kThreads;
     int per_cu = 0;

@@ -322,6 +322,20 @@ ATTN_HD bool bwd_kv_edge(int kb, int w, int u, int T, bool causal) {
     const int q0 = (bwd_first_qtile(kb, causal) + u) * kBwdBlockQ;
     return (causal && q0 < kw0 + 31) || q0 + kBwdBlockQ > T;
 }
+// The single-kernel backward (dQ added with atomics) shares the dK/dV
+// kernel's work map and adds two LDS tiles holding dS^T of the workgroup's
+// key block for the current query tile (row = key, column = query, swz_b).
+// Wave w writes rows 32w .. 32w + 31 (tile w / 2); lane (ql, h) of half mt
+// writes its 4 packed values of register group g, queries 32mt + 8g + 4h ..
+// + 3 of key 32w + ql, as one 8-byte store.
+ATTN_HD int bwd_ds_byte(int w, int ql, int h, int mt, int g) {
+    return kTileBytes16 * (w >> 1) + b_elem_byte(32 * (w & 1) + ql, 32 * mt + 8 * g + 4 * h);
+}
+// Its dQ product: wave w owns the 32 x 32 output block of queries
+// 32 * bwd_dq_qhalf(w) .. and dims 32 * bwd_dq_dhalf(w) .. of the tile,
+// summed over the block's 128 keys.
+ATTN_HD int bwd_dq_qhalf(int w) { return w >> 1; }
+ATTN_HD int bwd_dq_dhalf(int w) { return w & 1; }
 // Wave w of the dQ kernel's query tile qt (queries qt * kBlockM + 32w ..
 // + 31) and key tile u of kBlockN16 keys: how many key tiles the wave sees
 // (causal: none past its last query), and whether tile u needs masks (a key

@@ -32,6 +32,14 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       float* delta, int BH, int T, int causal, float c, float scale,
                       bool negate, int dt, hipStream_t stream);
 
+// Backward pass in one main kernel (16-bit dtypes): delta into `delta` and
+// zeros into `dq_acc` ([BH, T, 64] float32), then dK/dV with the dQ sums
+// added to dq_acc by atomics, then dq = scale * dq_acc.
+hipError_t launch_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             float* delta, float* dq_acc, int BH, int T, int causal, float c,
+                             float scale, bool negate, int dt, hipStream_t stream);
+
 // Decode: Tq queries against a Tk-token cache, split over the keys into
 // o_part [BH*Tq, nsplit, 64] and lse_part [BH*Tq, nsplit] (float32), then
 // merged; the split is decode_plan (fused_layout.h).
@@ -55,11 +63,13 @@ constexpr int kBwdKernels = 10;
 constexpr int kDecodeKernels = 6;
 constexpr int kHdKernels = 8;
 constexpr int kRecurrenceKernels = 16;
+constexpr int kBwdAtomicKernels = 8;
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
 const void* decode_kernel_ptr(int index);
 const void* hd_kernel_ptr(int index);
 const void* recurrence_kernel_ptr(int index);
+const void* bwd_atomic_kernel_ptr(int index);
 
 }  // namespace attn

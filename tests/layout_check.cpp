@@ -423,6 +423,9 @@ static void check_bwd_access(int BH, int T, bool causal) {
         int bh, kb;
         bwd_kv_tile_of(b, nkb * BH, nkb, causal, &bh, &kb);
         CHECK(bh >= 0 && bh < BH, "bwd slice");
+        // the single-kernel backward's K block: two 64-row tiles
+        tile_ok((long)kb * kBwdBlockKV, "bwd_kvq K block");
+        tile_ok((long)kb * kBwdBlockKV + 64, "bwd_kvq K block");
         for (int u = bwd_first_qtile(kb, causal); u < nqt; ++u) {
             const long q0 = (long)u * kBwdBlockQ;
             tile_ok(q0, "bwd_kv");
@@ -547,6 +550,95 @@ static void check_bwd_q_edges() {
                     // every visible key tile is among the first nw
                     if (wq0 < T) CHECK(nw >= 1, "bwd q: a wave with rows sees no tile");
                 }
+            }
+        }
+}
+
+// The single-kernel backward (dQ by atomics): the dS^T writes cover the two
+// LDS tiles once with the right (key, query); the dQ product's two
+// transposed reads pair the same key in every reduction slot and cover the
+// block's 128 keys; the four waves' output blocks cover the 64 x 64 tile
+// once; and every atomic's row stays inside the slice.
+static void check_bwd_atomic_layout() {
+    std::vector<int> cov(128 * 64, 0);
+    for (int w = 0; w < kWaves; ++w)
+        for (int l = 0; l < 64; ++l)
+            for (int mt = 0; mt < 2; ++mt)
+                for (int g = 0; g < 4; ++g) {
+                    const int ql = l & 31, h = l >> 5;
+                    const int b = bwd_ds_byte(w, ql, h, mt, g);
+                    CHECK(b % 8 == 0 && b >= 0 && b + 8 <= 2 * kTileBytes16, "dS^T write range");
+                    for (int e = 0; e < 4; ++e) {
+                        const int tile = b / kTileBytes16;
+                        int row, dim;
+                        decode_b(b % kTileBytes16 + 2 * e, &row, &dim);
+                        const int key = 64 * tile + row;
+                        // packed value e of group g is accumulator register
+                        // 4g + e: query 32mt + acc_row(4g + e, h)
+                        CHECK(key == 32 * w + ql, "dS^T write key");
+                        CHECK(dim == 32 * mt + acc_row(4 * g + e, h), "dS^T write query");
+                        cov[key * 64 + dim]++;
+                    }
+                }
+    for (int x = 0; x < 128 * 64; ++x) CHECK(cov[x] == 1, "dS^T element written %d times", cov[x]);
+    // reduction slots: both operands come from btr of a 64-row tile (ks >> 2)
+    // at step ks & 3 with the same lane pattern; the row (key) each slot holds
+    std::vector<int> keys(128, 0);
+    for (int ks = 0; ks < 8; ++ks)
+        for (int h = 0; h < 2; ++h)
+            for (int s = 0; s < 8; ++s) {
+                const int key = 64 * (ks >> 2) + 16 * (ks & 3) + 8 * (s / 4) + 4 * h + s % 4;
+                keys[key]++;
+            }
+    for (int x = 0; x < 128; ++x) CHECK(keys[x] == 1, "dQ product key %d summed %d times", x, keys[x]);
+    std::vector<int> out(64 * 64, 0);
+    for (int w = 0; w < kWaves; ++w)
+        for (int l = 0; l < 64; ++l)
+            for (int r = 0; r < 16; ++r) {
+                const int qi = 32 * bwd_dq_qhalf(w) + acc_row(r, l >> 5);
+                const int d = 32 * bwd_dq_dhalf(w) + (l & 31);
+                CHECK(qi >= 0 && qi < 64 && d >= 0 && d < 64, "dQ block range");
+                if (qi >= 0 && qi < 64 && d >= 0 && d < 64) out[qi * 64 + d]++;
+            }
+    for (int x = 0; x < 64 * 64; ++x) CHECK(out[x] == 1, "dQ element owned %d times", out[x]);
+}
+static void check_bwd_atomic_rows(int T, bool causal) {
+    const int nkb = (T + kBwdBlockKV - 1) / kBwdBlockKV;
+    const int nqt = (T + kBwdBlockQ - 1) / kBwdBlockQ;
+    for (int kb = 0; kb < nkb; ++kb)
+        for (int u = 0; u < nqt - bwd_first_qtile(kb, causal); ++u)
+            for (int w = 0; w < kWaves; ++w) {
+                const int qb = (bwd_first_qtile(kb, causal) + u) * kBwdBlockQ + 32 * bwd_dq_qhalf(w);
+                for (int h = 0; h < 2; ++h)
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = std::min(qb + acc_row(r, h), T - 1);
+                        CHECK(row >= 0 && row < T, "dQ atomic row %d outside T %d", row, T);
+                    }
+            }
+}
+// The wait at the top of tile u lets 16 operations stay pending; with
+// vector-memory operations completing in issue order this covers tile u's
+// loads when at least 16 operations were issued after them. Model each wave's
+// issue order (K block and tile 0 drained before the loop; loads of tile
+// u + 1 at the top of tile u; 16 atomics at its end) and check it.
+static void check_bwd_atomic_waits() {
+    for (int n = 1; n <= 40; ++n)
+        for (int w = 0; w < kWaves; ++w) {
+            const int L = 4 + (w < 2 ? 1 : 0);
+            std::vector<int> tile_of_op;  // -1: atomic, else the tile loaded
+            for (int u = 0; u < n; ++u) {
+                if (u > 0) {
+                    // ops issued after the last load of tile u
+                    int last = -1;
+                    for (int i = 0; i < (int)tile_of_op.size(); ++i)
+                        if (tile_of_op[i] == u) last = i;
+                    CHECK(last >= 0, "tile %d loads never issued", u);
+                    const int after = (int)tile_of_op.size() - 1 - last;
+                    CHECK(after >= 16, "wait at tile %d of %d: only %d ops after its loads", u, n, after);
+                }
+                if (u + 1 < n)
+                    for (int i = 0; i < L; ++i) tile_of_op.push_back(u + 1);
+                for (int i = 0; i < 16; ++i) tile_of_op.push_back(-1);
             }
         }
 }
@@ -709,6 +801,10 @@ int main() {
     check_bwd_layout();
     check_bwd_kv_edges();
     check_bwd_q_edges();
+    check_bwd_atomic_layout();
+    check_bwd_atomic_waits();
+    for (int T = 1; T <= 700; T += (T < 300 ? 1 : 23))
+        for (int causal = 0; causal < 2; ++causal) check_bwd_atomic_rows(T, causal);
     check_head_dim<32>();
     check_head_dim<128>();
     for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})

@@ -94,9 +94,9 @@ def test_naive_rejects_invalid(lib, kw, status):
     assert naive(lib, **kw) == status
 
 
-def bwd(lib, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1,
+def bwd(lib, entry, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1,
         H=1, T=8, D=64, dtype=1, scale=0.125):
-    return lib.attn_bwd_stream(q, FAKE, FAKE, o, FAKE, lse, dq, FAKE, FAKE, ws,
+    return getattr(lib, entry)(q, FAKE, FAKE, o, FAKE, lse, dq, FAKE, FAKE, ws,
                                ws_bytes, B, H, T, D, 1, scale, dtype, None)
 
 
@@ -110,8 +110,21 @@ def bwd(lib, q=FAKE, o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1,
     (dict(B=4096, H=2048, T=256), -2),  # grid beyond one launch
     (dict(T=1 << 25), -2),  # one slice over 4 GiB
 ])
-def test_bwd_rejects_invalid(lib, kw, status):
-    assert bwd(lib, **kw) == status
+@pytest.mark.parametrize("entry", ["attn_bwd_stream", "attn_bwd_atomic_stream"])
+def test_bwd_rejects_invalid(lib, entry, kw, status):
+    assert bwd(lib, entry, **kw) == status
+
+
+def test_bwd_atomic_workspace_bytes(lib):
+    """delta (padded to 256 bytes) followed by the float32 copy of dQ; a
+    workspace one byte short is refused."""
+    for B, H, T in [(1, 1, 1), (2, 3, 1000), (4, 12, 8192)]:
+        rows = -(-B * H * T * 4 // 256) * 256
+        need = osa.attn_bwd_atomic_workspace_bytes(B, H, T)
+        assert need == rows + B * H * T * 64 * 4
+        assert bwd(lib, "attn_bwd_atomic_stream", B=B, H=H, T=T, ws_bytes=need - 1) == -1
+    assert osa.attn_bwd_atomic_workspace_bytes(0, 1, 1) == 0
+    assert osa.attn_bwd_atomic_workspace_bytes(1 << 30, 1 << 30, 1 << 30) == 0
 
 
 def test_bwd_workspace_and_flops():
@@ -272,7 +285,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 49
+    assert n == 57
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None
