@@ -28,15 +28,65 @@ struct RowState {
     float m, mc, l;
 };
 
-// The online-softmax step of one tile: mask (EDGE tiles: keys >= T and,
-// causal, keys after the row), row maximum, the lazy reference update (with
-// the rescale of O and l when some row's maximum jumps by more than
-// kLazyLog2), the weights p = exp2(s*c - m*c) rounded into the P fragment,
-// and their sum into l.
+// The online-softmax step of one tile: the weights p = exp2(s*c - m*c)
+// rounded into the P fragment and their sum into l, with the lazy reference
+// update (O and l rescaled by exp2(m_old - m_new) when some row's maximum
+// jumps by more than kLazyLog2). EDGE tiles (keys >= T and, causal, keys
+// after the row, set to -inf) take the row maximum first. Unmasked tiles
+// take the weights first against the current reference and need no
+// maximum: a lane's 32 weights are each at most their sum t, so t <= 2^8 in
+// every lane keeps every weight within the bound (an overflow to inf fails
+// the test too); otherwise (rare) the maximum is taken, the reference moved
+// if it jumped by more than kLazyLog2, and the weights made again from S,
+// which is still in registers. Both orders take the same decisions, so
+// the results are the same bits.
 template <int DT, bool CAUSAL, bool EDGE, int NO>
 __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
                                     v16f32 (&oacc)[NO], RowState& st, float c,
                                     int k0, int T, int my_q, int hh) {
+    auto weights = [&](float mc) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int nt = ks >> 1, r0 = (ks & 1) * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = s[nt][r0 + 2 * i], x1 = s[nt][r0 + 2 * i + 1];
+                float p0 = fast_exp2(fmaf(x0, c, -mc));
+                float p1 = fast_exp2(fmaf(x1, c, -mc));
+                if (EDGE) {
+                    if (x0 == -INFINITY) p0 = 0.f;
+                    if (x1 == -INFINITY) p1 = 0.f;
+                }
+                pf[ks][i] = pack2<DT>(p0, p1);
+                if (i & 1)
+                    t1 = sum2<DT>(pf[ks][i], t1);
+                else
+                    t0 = sum2<DT>(pf[ks][i], t0);
+            }
+        }
+        return t0 + t1;
+    };
+    auto rescale = [&]() {
+        float mx = s[0][0];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+        mx = halves_max(mx);
+        if (__builtin_amdgcn_ballot_w64(mx * c - st.mc > kLazyLog2) != 0) {
+            const float m_new = fmaxf(st.m, mx);
+            const float mc_new = m_new * c;
+            const float corr = fast_exp2(st.mc - mc_new);
+            st.m = m_new;
+            st.mc = mc_new;
+            st.l *= corr;
+#pragma unroll
+            for (int mt = 0; mt < NO; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
+        }
+    };
     if (EDGE) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -45,47 +95,16 @@ __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
                 const int key = k0 + 32 * nt + acc_row(r, hh);
                 if (key >= T || (CAUSAL && key > my_q)) s[nt][r] = -INFINITY;
             }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
-    mx = halves_max(mx);
-    // a fully masked row has mx = -inf and never asks for a rescale
-    if (__builtin_amdgcn_ballot_w64(mx * c - st.mc > kLazyLog2) != 0) {
-        const float m_new = fmaxf(st.m, mx);
-        const float mc_new = m_new * c;
-        const float corr = fast_exp2(st.mc - mc_new);
-        st.m = m_new;
-        st.mc = mc_new;
-        st.l *= corr;
-#pragma unroll
-        for (int mt = 0; mt < NO; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
-    }
-    float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int nt = ks >> 1, r0 = (ks & 1) * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = s[nt][r0 + 2 * i], x1 = s[nt][r0 + 2 * i + 1];
-            float p0 = fast_exp2(fmaf(x0, c, -st.mc));
-            float p1 = fast_exp2(fmaf(x1, c, -st.mc));
-            if (EDGE) {  // masked keys weigh exactly 0 (also for c = 0)
-                if (x0 == -INFINITY) p0 = 0.f;
-                if (x1 == -INFINITY) p1 = 0.f;
-            }
-            pf[ks][i] = pack2<DT>(p0, p1);
-            if (i & 1)
-                t1 = sum2<DT>(pf[ks][i], t1);
-            else
-                t0 = sum2<DT>(pf[ks][i], t0);
+        rescale();
+        st.l += weights(st.mc);
+    } else {
+        float t = weights(st.mc);
+        if (__builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0) {
+            rescale();
+            t = weights(st.mc);
         }
+        st.l += t;
     }
-    st.l += t0 + t1;
 }
 
 }  // namespace attn
