@@ -311,7 +311,10 @@ const char* attn_kernel_name(int kernel);
 int attn_kernel_attributes(int kernel, attn_kernel_attr* out);
 
 /* Tile geometry of the fused path, for traffic arithmetic and tests:
- * queries per workgroup and keys per LDS tile for `dtype`. */
+ * queries per workgroup and keys per LDS tile for `dtype`. A float32 call
+ * whose grid would have fewer than 256 such workgroups (B*H*ceil(T/128))
+ * runs a kernel that splits the keys among the waves of a workgroup of 32
+ * query rows instead; attn_traffic_bytes counts that kernel's tiles. */
 int attn_fused_tile(int dtype, int* block_m, int* block_n);
 
 #ifdef __cplusplus

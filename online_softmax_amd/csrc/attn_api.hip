@@ -355,6 +355,8 @@ int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
         // K and V rows each query tile loads (rows >= T are never fetched)
         int bm, bn;
         attn_fused_tile(dtype, &bm, &bn);
+        // fp32 on a small grid runs the key-split kernel on 32-row tiles
+        if (dtype == ATTN_F32 && attn::fwd32_split((long long)bh, T)) bm = attn::kSplitRows;
         const int nq = (T + bm - 1) / bm;
         uint64_t kv_rows = 0;
         for (int qt = 0; qt < nq; ++qt) {
@@ -407,6 +409,7 @@ const char* attn_kernel_name(int kernel) {
         "fused_fwd16<bf16, causal>", "fused_fwd16<bf16, full>",
         "fused_fwd16<f16, causal>",  "fused_fwd16<f16, full>",
         "fused_fwd32<causal>",       "fused_fwd32<full>",
+        "fused_fwd32_split<causal>", "fused_fwd32_split<full>",
         "naive_scores",              "naive_softmax",
         "naive_weighted_v",
         "bwd_delta16<bf16>",         "bwd_kv16<bf16, causal>",
@@ -456,7 +459,8 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     if (e != hipSuccess) return hip_fail(e);
     // threads per workgroup of the kernel's launches: the recurrence's
     // kernel i runs i + 1 waves
-    const int threads = kernel >= bat0     ? attn::kThreads
+    const int threads = kernel >= 6 && kernel < naive0 ? attn::kSplitThreads
+                        : kernel >= bat0     ? attn::kThreads
                         : kernel >= rec0 + 8 ? 64
                         : kernel >= rec0   ? 64 * (kernel - rec0 + 1)
                                            : attn::kThreads;

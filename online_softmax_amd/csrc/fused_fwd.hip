@@ -26,6 +26,10 @@
 //    (fp32 inputs: v_mfma_f32_32x32x2_f32 from VGPR-staged, padded LDS
 //    tiles), fp32 accumulation; the 16-bit main loop is a three-stage
 //    software pipeline with a lazily moved softmax reference.
+//  - fp32 on grids too small to fill the CUs (one head of a few thousand
+//    tokens): eight waves share 32 query rows and split the key tiles among
+//    them, each staging its own tiles, and merge their partial results
+//    through LDS at the end (fused_fwd32_split).
 //  - Row max / row sum: in-lane, then one v_permlane32_swap between halves.
 //  - Masks only on the diagonal and ragged tiles; tiles a whole wave cannot
 //    see are skipped by that wave (it still joins every barrier).
@@ -588,6 +592,163 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd32(
     }
 }
 
+// fp32 inputs, small grids: kSplitWaves waves share 32 query rows and split
+// the key tiles among them (wave w: tiles w, w + kSplitWaves, ...), each with
+// its own LDS tile, no barrier until the end; then the partial results merge
+// by the online-softmax combination O = sum_w 2^(m_w c - m c) O_w over
+// sum_w 2^(m_w c - m c) l_w, m the largest m_w.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kSplitThreads, 1) void fused_fwd32_split(
+    const float* __restrict__ q, const float* __restrict__ k,
+    const float* __restrict__ v, float* __restrict__ o,
+    float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
+    constexpr int BN = kBlockN32;
+    __shared__ __attribute__((aligned(16))) float lds[kSplitWaves][kSplitTileFloats];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+
+    int bh, qt;
+    tile_of(blockIdx.x, gridDim.x, nq, CAUSAL, &bh, &qt);
+    const int64_t base = (int64_t)bh * T * kHeadDim;
+    const float* kh = k + base;
+    const float* vh = v + base;
+    const int q0 = qt * kSplitRows;
+    const int my_q = q0 + ql;
+    const int n_tiles = key_tiles(qt, T, BN, CAUSAL, kSplitRows);
+    const int n_main = main_tiles(qt, T, BN, CAUSAL, kSplitRows);
+
+    v4f32 qf[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        v4u32 x = {0u, 0u, 0u, 0u};
+        if (my_q < T)
+            x = *(const v4u32*)(q + base + (int64_t)my_q * kHeadDim + q_col32(hh, g));
+        qf[g] = __builtin_bit_cast(v4f32, x ^ qsign);
+    }
+
+    // The wave stages its tiles alone: lane l does the work of threads
+    // l + 64 j (j < 4) of the 256-thread staging pattern.
+    float* const sk = lds[wave];
+    float* const sv = lds[wave] + kKTile32;
+    v4f32 kr[8], vr[8];
+    auto gload = [&](int kt) {
+        const int k0 = kt * BN;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = lane + 64 * j;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                int row, col;
+                k_stage32(t, i, &row, &col);
+                v4f32 x = {0.f, 0.f, 0.f, 0.f};
+                if (k0 + row < T) x = *(const v4f32*)(kh + (int64_t)(k0 + row) * kHeadDim + col);
+                kr[2 * j + i] = x;
+            }
+            int key0, dim0;
+            v_stage32(t, &key0, &dim0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                v4f32 x = {0.f, 0.f, 0.f, 0.f};
+                if (k0 + key0 + e < T)
+                    x = *(const v4f32*)(vh + (int64_t)(k0 + key0 + e) * kHeadDim + dim0);
+                vr[2 * j + e] = x;
+            }
+        }
+    };
+    // LDS reads and writes of one wave complete in order, so the next tile
+    // may overwrite the one the wave has just read without a barrier.
+    auto lstore = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = lane + 64 * j;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                int row, col;
+                k_stage32(t, i, &row, &col);
+                *(v4f32*)&sk[k_lds32(row, col)] = kr[2 * j + i];
+            }
+            int key0, dim0;
+            v_stage32(t, &key0, &dim0);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float2 w;
+                w.x = vr[2 * j][d];
+                w.y = vr[2 * j + 1][d];
+                *(float2*)&sv[v_lds32(dim0 + d, key0)] = w;
+            }
+        }
+    };
+
+    v16f32 oacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
+    RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
+
+    auto step = [&](int kt, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        const bool more = kt + kSplitWaves < n_tiles;
+        if (more) gload(kt + kSplitWaves);
+        tile32<CAUSAL, EDGE>(sk, sv, qf, oacc, st, c, kt * BN, T, my_q, ql, hh);
+        if (more) lstore();
+    };
+    int kt = wave;
+    if (kt < n_tiles) {
+        gload(kt);
+        lstore();
+    }
+    for (; kt < n_main; kt += kSplitWaves) step(kt, std::integral_constant<bool, false>());
+    for (; kt < n_tiles; kt += kSplitWaves) step(kt, std::integral_constant<bool, true>());
+
+    // Merge: each wave's partial O (rows = queries, stride kMergeStride32),
+    // reference m*c and denominator into LDS, then thread t finishes dims
+    // 4 (t % 16) .. + 3 of row t / 16.
+    __syncthreads();
+    float* const obuf = &lds[0][0];
+    float* const mlbuf = obuf + kSplitWaves * kSplitRows * kMergeStride32;
+    {
+        float* ow = obuf + wave * kSplitRows * kMergeStride32 + ql * kMergeStride32;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ow[32 * mt + acc_row(r, hh)] = oacc[mt][r];
+        const float lt = halves_sum(st.l);
+        if (hh == 0) {
+            mlbuf[2 * (wave * kSplitRows + ql)] = st.mc;
+            mlbuf[2 * (wave * kSplitRows + ql) + 1] = lt;
+        }
+    }
+    __syncthreads();
+    const int row = tid >> 4, d0 = 4 * (tid & 15);
+    float mcmax = mlbuf[2 * row];
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) mcmax = fmaxf(mcmax, mlbuf[2 * (w * kSplitRows + row)]);
+    float den = 0.f;
+    v4f32 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+        const float a = fast_exp2(mlbuf[2 * (w * kSplitRows + row)] - mcmax);
+        den = fmaf(a, mlbuf[2 * (w * kSplitRows + row) + 1], den);
+        const float* ow = obuf + (w * kSplitRows + row) * kMergeStride32 + d0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[i] = fmaf(a, ow[i], num[i]);
+    }
+    if (q0 + row < T) {
+        const float inv = 1.0f / den;
+        v4f32 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = num[i] * inv;
+        *(v4f32*)(o + base + (int64_t)(q0 + row) * kHeadDim + d0) = w;
+        if (lse != nullptr && (tid & 15) == 0)
+            lse[(int64_t)bh * T + q0 + row] = (mcmax + log2f(den)) * kLn2;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers and the kernel table.
 // ---------------------------------------------------------------------------
@@ -595,14 +756,20 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, void* o,
                         float* lse, int BH, int T, int causal, float c,
                         bool negate_q, int dt, hipStream_t stream) {
     if (dt == ATTN_DT_F32) {
-        const int nq = (T + kBlockM - 1) / kBlockM;
-        const dim3 grid((unsigned)(nq * BH));
-        const dim3 block(kThreads);
         const uint32_t sign = negate_q ? 0x80000000u : 0u;
-        auto fn = causal ? fused_fwd32<true> : fused_fwd32<false>;
-        hipLaunchKernelGGL(fn, grid, block, 0, stream, (const float*)q,
-                           (const float*)k, (const float*)v, (float*)o, lse, T,
-                           nq, c, sign);
+        if (fwd32_split(BH, T)) {
+            const int nq = (T + kSplitRows - 1) / kSplitRows;
+            auto fn = causal ? fused_fwd32_split<true> : fused_fwd32_split<false>;
+            hipLaunchKernelGGL(fn, dim3((unsigned)(nq * BH)), dim3(kSplitThreads), 0, stream,
+                               (const float*)q, (const float*)k, (const float*)v, (float*)o,
+                               lse, T, nq, c, sign);
+        } else {
+            const int nq = (T + kBlockM - 1) / kBlockM;
+            auto fn = causal ? fused_fwd32<true> : fused_fwd32<false>;
+            hipLaunchKernelGGL(fn, dim3((unsigned)(nq * BH)), dim3(kThreads), 0, stream,
+                               (const float*)q, (const float*)k, (const float*)v, (float*)o,
+                               lse, T, nq, c, sign);
+        }
     } else {
         const int nq = (T + kBlockM - 1) / kBlockM;
         const dim3 grid((unsigned)(nq * BH));
@@ -633,6 +800,8 @@ const void* fused_kernel_ptr(int index) {
         case 3: return (const void*)fused_fwd16<ATTN_DT_F16, false>;
         case 4: return (const void*)fused_fwd32<true>;
         case 5: return (const void*)fused_fwd32<false>;
+        case 6: return (const void*)fused_fwd32_split<true>;
+        case 7: return (const void*)fused_fwd32_split<false>;
         default: return nullptr;
     }
 }

@@ -375,6 +375,26 @@ ATTN_HD void decode_plan(int BH, int Tq, int Tk, int* nsplit, int* chunk) {
 // Q fragment of lane-half h for reduction step ks: dims 16*ks + 8*h .. +7.
 ATTN_HD int q_col16(int h, int ks) { return 16 * ks + 8 * h; }
 
+// ---- fp32 forward for small grids -----------------------------------------
+// With fewer 128-row workgroups than CUs (one head of a few thousand tokens),
+// the fp32 forward splits the keys inside a workgroup instead: kSplitWaves
+// waves share 32 query rows, wave w takes key tiles w, w + kSplitWaves, ...
+// and stages them in LDS of its own, and the waves' partial (O, m, l) merge
+// through LDS at the end.
+constexpr int kSplitWaves = 8;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+constexpr int kSplitRows = 32;         // query rows per workgroup
+constexpr int kSplitMinGrid = 256;     // 128-row workgroups below which it is used
+constexpr int kSplitTileFloats = kKTile32 + kVTile32;   // one wave's K and V^T tile
+constexpr int kMergeStride32 = 65;     // floats per row of a wave's partial O
+ATTN_HD bool fwd32_split(long long BH, int T) {
+    return (long long)((T + kBlockM - 1) / kBlockM) * BH < kSplitMinGrid;
+}
+static_assert(kSplitWaves * kSplitTileFloats * 4 <= 160 * 1024,
+              "the split kernel's per-wave tiles must fit the LDS");
+static_assert(kSplitWaves * kSplitRows * (kMergeStride32 + 2) <= kSplitWaves * kSplitTileFloats,
+              "the merge area must fit in the tiles' LDS");
+
 // ---- fp32 staging ----------------------------------------------------------
 // K tile: 32 keys x 64 dims = 512 chunks of 16 B; chunks t and t + 256.
 ATTN_HD void k_stage32(int t, int i, int* row, int* col) {

@@ -57,7 +57,7 @@ hipError_t launch_recurrence(const float* q, const float* k, const float* v, con
                              float* y, int B, int T, int H, int D, hipStream_t stream);
 
 // Kernel table for attribute queries.
-constexpr int kFusedKernels = 6;
+constexpr int kFusedKernels = 8;
 constexpr int kNaiveKernels = 3;
 constexpr int kBwdKernels = 10;
 constexpr int kDecodeKernels = 6;

@@ -643,6 +643,59 @@ static void check_bwd_atomic_waits() {
         }
 }
 
+// The fp32 key-split kernel: a wave's 4 x 256-thread staging covers its K
+// tile (32 keys x 64 dims) and V^T tile once, inside its LDS slot; the
+// waves' tiles (w, w + 8, ...) cover each key tile once, masked tiles being
+// exactly those from main_tiles on; the merge area's rows stay inside the
+// tiles' LDS.
+static void check_fwd32_split() {
+    std::vector<int> kc(32 * 64, 0), vc(32 * 64, 0);
+    for (int lane = 0; lane < 64; ++lane)
+        for (int j = 0; j < 4; ++j) {
+            const int t = lane + 64 * j;
+            for (int i = 0; i < 2; ++i) {
+                int row, col;
+                k_stage32(t, i, &row, &col);
+                CHECK(row >= 0 && row < 32 && col >= 0 && col + 4 <= 64, "split K stage");
+                CHECK(k_lds32(row, col) + 4 <= kKTile32, "split K slot");
+                for (int e = 0; e < 4; ++e) kc[row * 64 + col + e]++;
+            }
+            int key0, dim0;
+            v_stage32(t, &key0, &dim0);
+            CHECK(key0 >= 0 && key0 + 2 <= 32 && dim0 >= 0 && dim0 + 4 <= 64, "split V stage");
+            for (int d = 0; d < 4; ++d) {
+                CHECK(v_lds32(dim0 + d, key0) + 2 <= kVTile32, "split V slot");
+                for (int e = 0; e < 2; ++e) vc[(key0 + e) * 64 + dim0 + d]++;
+            }
+        }
+    for (int x = 0; x < 32 * 64; ++x) CHECK(kc[x] == 1 && vc[x] == 1, "split staging coverage");
+    CHECK(kSplitWaves * kSplitRows * kMergeStride32 + 2 * kSplitWaves * kSplitRows <=
+              kSplitWaves * kSplitTileFloats, "split merge area");
+    for (int causal = 0; causal < 2; ++causal)
+        for (int T = 1; T <= 700; T += (T < 200 ? 1 : 29)) {
+            const int nq = (T + kSplitRows - 1) / kSplitRows;
+            for (int qt = 0; qt < nq; ++qt) {
+                const int n = key_tiles(qt, T, kBlockN32, causal, kSplitRows);
+                const int nm = main_tiles(qt, T, kBlockN32, causal, kSplitRows);
+                std::vector<int> seen(n, 0);
+                for (int w = 0; w < kSplitWaves; ++w)
+                    for (int kt = w; kt < n; kt += kSplitWaves) seen[kt]++;
+                for (int kt = 0; kt < n; ++kt) CHECK(seen[kt] == 1, "split tile %d owned %d times", kt, seen[kt]);
+                // a tile before main_tiles needs no mask for any of the 32 rows
+                for (int kt = 0; kt < nm; ++kt)
+                    CHECK(kt * 32 + 31 < T && (!causal || kt * 32 + 31 <= qt * kSplitRows),
+                          "split main tile %d of qt %d T %d needs a mask", kt, qt, T);
+                // every key some row of the tile sees lies in the first n tiles
+                const int last_row = std::min(T - 1, qt * kSplitRows + kSplitRows - 1);
+                const int last_key = causal ? last_row : T - 1;
+                CHECK(last_key < n * 32, "split tiles miss key %d", last_key);
+            }
+        }
+    for (int BH : {1, 3, 6, 48, 64})
+        for (int T : {1, 256, 1000, 1024, 4096, 8192})
+            CHECK(fwd32_split(BH, T) == (((T + 127) / 128) * BH < 256), "split selection");
+}
+
 // Other head dims: direct-load coverage, K fragment decode, strides and bank
 // conflicts, and the transposed V reads simulated with the hardware rule
 // against the P fragment's key order, for D = 32 and 128.
@@ -802,6 +855,7 @@ int main() {
     check_bwd_kv_edges();
     check_bwd_q_edges();
     check_bwd_atomic_layout();
+    check_fwd32_split();
     check_bwd_atomic_waits();
     for (int T = 1; T <= 700; T += (T < 300 ? 1 : 23))
         for (int causal = 0; causal < 2; ++causal) check_bwd_atomic_rows(T, causal);

@@ -111,6 +111,25 @@ def test_noncausal_fp32_two_by_three(gpu_lib, T):
     check_full(gpu_lib, q, k, v, False, 0.125, "f32", f"full_b2h3_t{T}_f32")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1000, 1024])
+def test_fp32_large_grid(gpu_lib, T, causal):
+    """Enough heads (4 x 16) that the fp32 forward runs the 128-row kernel;
+    the single-head and 2 x 3 cases above run the key-split kernel."""
+    assert not ((T + 127) // 128 * 64 < 256)
+    q, k, v = make_qkv(4, 16, T, D, "f32", 1300 + T)
+    check_full(gpu_lib, q, k, v, causal, 0.125, "f32", f"b4h16_t{T}_f32_c{int(causal)}")
+
+
+@pytest.mark.parametrize("T", [31, 32, 33, 300])
+def test_fp32_split_ragged_and_tiny(gpu_lib, T):
+    """The key-split kernel with fewer key tiles than waves (waves with no
+    tile merge as zero weight), at and around one 32-key tile."""
+    q, k, v = make_qkv(1, 2, T, D, "f32", 1400 + T)
+    check_full(gpu_lib, q, k, v, True, 0.125, "f32", f"split_t{T}_c")
+    check_full(gpu_lib, q, k, v, False, 0.125, "f32", f"split_t{T}_f")
+
+
 # --- 16-bit ragged lengths ------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
