@@ -188,61 +188,84 @@ __global__ __launch_bounds__(64 * NI) void gated_recurrence32(
 
     // thread tid carries elements tid + n * kThreadsR of a block: tensor x,
     // step u, element i (< D only); loaded into registers, then written to
-    // their LDS slots
+    // their LDS slots. The split of an element index into (x, u, i) is the
+    // same for every block, so it is made once: the element's address in
+    // block 0, its step u (-1: the thread has no element n) and its slot.
     const int per_block = 4 * kRecSteps * D;
+    const float* lp[kPerThread];
+    int lu[kPerThread], lpos[kPerThread];
+#pragma unroll
+    for (int n = 0; n < kPerThread; ++n) {
+        const int e = tid + n * kThreadsR;
+        lp[n] = src[0];
+        lu[n] = -1;
+        lpos[n] = 0;
+        if (e < per_block) {
+            const int x = e / (kRecSteps * D);
+            const int rem = e - x * (kRecSteps * D);
+            const int u = rem / D;
+            const int i = rem - u * D;
+            lp[n] = src[x] + (int64_t)u * step_stride + i;
+            lu[n] = u;
+            lpos[n] = (x * kRecSteps + u) * kRecSlots + (x < 2 ? 8 * (i & 7) + (i >> 3) : i);
+        }
+    }
+    const int64_t block_stride = (int64_t)kRecSteps * step_stride;
     float buf[kPerThread];
     auto load = [&](int blk) {
 #pragma unroll
         for (int n = 0; n < kPerThread; ++n) {
-            const int e = tid + n * kThreadsR;
-            float val = 0.f;
-            if (e < per_block) {
-                const int x = e / (kRecSteps * D);
-                const int rem = e - x * (kRecSteps * D);
-                const int u = rem / D;
-                const int t = blk * kRecSteps + u;
-                if (t < T) val = src[x][(int64_t)t * step_stride + (rem - u * D)];
-            }
-            buf[n] = val;
+            const int t = blk * kRecSteps + lu[n];
+            buf[n] = (lu[n] >= 0 && t < T) ? lp[n][blk * block_stride] : 0.f;
         }
     };
     auto stage = [&](int slot) {
+        float* st = &lds[slot][0][0][0];
 #pragma unroll
-        for (int n = 0; n < kPerThread; ++n) {
-            const int e = tid + n * kThreadsR;
-            if (e < per_block) {
-                const int x = e / (kRecSteps * D);
-                const int rem = e - x * (kRecSteps * D);
-                const int u = rem / D;
-                const int i = rem - u * D;
-                const int pos = x < 2 ? 8 * (i & 7) + (i >> 3) : i;
-                lds[slot][x][u][pos] = buf[n];
-            }
-        }
+        for (int n = 0; n < kPerThread; ++n)
+            if (lu[n] >= 0) st[lpos[n]] = buf[n];
     };
 
     float S[NI];
 #pragma unroll
     for (int r = 0; r < NI; ++r) S[r] = 0.f;
+    // One step's inputs as the lane reads them: its 8 rows of q and of k,
+    // v and the gate of its column. The next step's are read before this
+    // step computes, so LDS latency hides behind the arithmetic.
+    struct StepIn {
+        float4 q0, q1, k0, k1;
+        float v, g;
+    };
+    auto read = [&](int slot, int u, StepIn& x) {
+        const float4* qrow = (const float4*)&lds[slot][0][u][8 * g];
+        const float4* krow = (const float4*)&lds[slot][1][u][8 * g];
+        x.q0 = qrow[0];
+        x.q1 = qrow[1];
+        x.k0 = krow[0];
+        x.k1 = krow[1];
+        x.v = lds[slot][2][u][j];
+        x.g = lds[slot][3][u][j];
+    };
     auto compute = [&](int slot, int t0) {
-#pragma unroll 4
+        StepIn cur, nxt;
+        read(slot, 0, cur);
+#pragma unroll
         for (int u = 0; u < kRecSteps; ++u) {
-            const float4* qrow = (const float4*)&lds[slot][0][u][8 * g];
-            const float4* krow = (const float4*)&lds[slot][1][u][8 * g];
-            const float4 q0 = qrow[0], q1 = qrow[1], k0 = krow[0], k1 = krow[1];
-            const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float vj = lds[slot][2][u][j];
-            const float gj = lds[slot][3][u][j];
+            if (u + 1 < kRecSteps) read(slot, u + 1, nxt);
+            const float qv[8] = {cur.q0.x, cur.q0.y, cur.q0.z, cur.q0.w,
+                                 cur.q1.x, cur.q1.y, cur.q1.z, cur.q1.w};
+            const float kv[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
+                                 cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < NI; ++r) {
-                S[r] = fmaf(gj, S[r], kv[r] * vj);
+                S[r] = fmaf(cur.g, S[r], kv[r] * cur.v);
                 acc = fmaf(qv[r], S[r], acc);
             }
             acc = sum8(acc);
             const int t = t0 + u;
             if (g == (u & 7) && col_ok && t < T) y[base + (int64_t)t * step_stride + j] = acc;
+            if (u + 1 < kRecSteps) cur = nxt;
         }
     };
 
