@@ -569,7 +569,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None,
                     help="a name from online_softmax_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-rows", type=int, default=196608,
