@@ -1,0 +1,105 @@
+"""A seeded sweep of random small shapes through every entry point, each
+against the double oracle with the bound its own tests use: the forward
+(every dtype; head dims 32, 64, 128 for 16-bit), both backward entry
+points, decode, and the gated recurrence. The shapes are drawn once from a
+fixed seed, so a failure names a reproducible case; they mix lengths on and
+off the tile sizes (32, 64, 128) with batch and head counts that change the
+grid's shape (and, for float32, which of its two kernels runs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from online_softmax_amd.inputs import make_gated, make_qkv
+from conftest import flush_print
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+_rng = np.random.Generator(np.random.PCG64(20261202))
+
+
+def _draw(n, t_max, bh_max=12):
+    out = []
+    for _ in range(n):
+        B = int(_rng.integers(1, 4))
+        H = int(_rng.integers(1, max(2, bh_max // B)))
+        T = int(_rng.integers(1, t_max))
+        causal = bool(_rng.integers(0, 2))
+        scale = float(_rng.choice([0.125, 0.07, -0.2, 0.3]))
+        out.append((B, H, T, causal, scale))
+    return out
+
+
+FWD_CASES = [(dt, D, *c) for dt, D in (("f32", 64), ("bf16", 64), ("f16", 64),
+                                        ("bf16", 32), ("f16", 128))
+             for c in _draw(4, 700)]
+BWD_CASES = [(dt, atomic, *c) for dt in ("bf16", "f16") for atomic in (False, True)
+             for c in _draw(3, 400)]
+DEC_CASES = [(dt, *c) for dt in ("bf16", "f16") for c in _draw(4, 900)]
+REC_CASES = [(int(_rng.integers(1, 3)), int(_rng.integers(1, 200)),
+              int(_rng.integers(1, 5)), int(_rng.integers(1, 65))) for _ in range(6)]
+
+
+def _max_err(got, want):
+    got = np.asarray(got, np.float64).reshape(want.shape)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.abs(got - want).max())
+
+
+@pytest.mark.parametrize("dtype,D,B,H,T,causal,scale", FWD_CASES)
+def test_sweep_forward(gpu_lib, dtype, D, B, H, T, causal, scale):
+    q, k, v = make_qkv(B, H, T, D, dtype, 9000 + T + 7 * D)
+    flush_print(f"[gpu] sweep fwd {dtype} D={D} {B}x{H}x{T} causal={causal} scale={scale}")
+    o, lse = gpu_lib.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal, scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, causal, scale)
+    bound = max(1e-5, 1e-5 * math.sqrt(T / 256.0)) if dtype == "f32" else 2e-2
+    assert _max_err(o.float().cpu().numpy(), ro) <= bound
+    assert _max_err(lse.cpu().numpy(), rl) <= bound
+
+
+@pytest.mark.parametrize("dtype,atomic,B,H,T,causal,scale", BWD_CASES)
+def test_sweep_backward(gpu_lib, dtype, atomic, B, H, T, causal, scale):
+    q, k, v = make_qkv(B, H, T, 64, dtype, 9100 + T)
+    (dout,) = make_qkv(B, H, T, 64, dtype, 9200 + T)[:1]
+    flush_print(f"[gpu] sweep bwd {dtype} atomic={atomic} {B}x{H}x{T} causal={causal} "
+                f"scale={scale}")
+    qd, kd, vd, dd = (x.to(DEV) for x in (q, k, v, dout))
+    o, lse = gpu_lib.attention(qd, kd, vd, causal, scale)
+    grads = gpu_lib.attention_backward(qd, kd, vd, o, lse, dd, causal, scale, atomic=atomic)
+    torch.cuda.synchronize()
+    want = oracle.attention_backward(q, k, v, dout, causal, scale)
+    for g, w in zip(grads, want):
+        assert _max_err(g.float().cpu().numpy(), w) <= 2e-2 * max(1.0, float(np.abs(w).max()))
+
+
+@pytest.mark.parametrize("dtype,B,H,Tk,causal,scale", DEC_CASES)
+def test_sweep_decode(gpu_lib, dtype, B, H, Tk, causal, scale):
+    Tq = int(1 + (Tk * 7919) % min(Tk, 40))  # 1 .. min(Tk, 40), from the case itself
+    (q,) = make_qkv(B, H, Tq, 64, dtype, 9300 + Tk)[:1]
+    _, k, v = make_qkv(B, H, Tk, 64, dtype, 9400 + Tk)
+    flush_print(f"[gpu] sweep decode {dtype} {B}x{H} Tq={Tq} Tk={Tk} causal={causal} "
+                f"scale={scale}")
+    o, lse = gpu_lib.attention_decode(q.to(DEV), k.to(DEV), v.to(DEV), causal, scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_kv(q, k, v, causal, scale)
+    assert _max_err(o.float().cpu().numpy(), ro) <= 2e-2
+    assert _max_err(lse.cpu().numpy(), rl) <= 2e-2
+
+
+@pytest.mark.parametrize("B,T,H,D", REC_CASES)
+def test_sweep_recurrence(gpu_lib, B, T, H, D):
+    q, k, v, g = make_gated(B, T, H, D, 9500 + T)
+    flush_print(f"[gpu] sweep recurrence {B}x{T}x{H}x{D}")
+    y = gpu_lib.gated_recurrence(*(x.to(DEV) for x in (q, k, v, g)))
+    torch.cuda.synchronize()
+    want = oracle.gated_recurrence(q, k, v, g)
+    mag = oracle.gated_recurrence(q.abs(), k.abs(), v.abs(), g)
+    t = np.arange(T, dtype=np.float64).reshape(1, T, 1, 1)
+    bound = 2.0 * (D + t + 2) * 2.0 ** -24 * mag
+    err = np.abs(y.cpu().numpy().astype(np.float64) - want)
+    assert np.all(err <= bound + 1e-30)
