@@ -278,7 +278,6 @@ __global__ __launch_bounds__(256) void decode_combine16(const float* __restrict_
         L += wave_sum(e);
         const int cnt = min(64, nsplit - s0);
         const uint32_t eb = __builtin_bit_cast(uint32_t, e);
-#pragma unroll 8
         for (int j = 0; j < cnt; ++j) {
             const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
             acc += ej * op[(int64_t)(s0 + j) * kHeadDim];
