@@ -140,6 +140,27 @@ def cpu_baseline(oracle, q, k, v, o, lse, w, nrows, seed):
         "max_abs_err_lse": err_l, "finite": finite}
 
 
+def oracle_single_core(oracle):
+    """The double oracle on one core for the page "attention.cu"'s one-head
+    case (256 tokens) and the largest of the two-sequence, three-head causal
+    cases (1000 tokens), whole, as that page times its CPU reference on one
+    core: seconds and GFLOP/s (4 D flop per visible query-key pair)."""
+    from online_softmax_amd.inputs import WORKLOADS, workload_qkv
+    out = []
+    for name in ("single_head_n256_f32", "causal_b2h3_t1000_f32"):
+        w = WORKLOADS[name]
+        q, k, v = (x.float().numpy() for x in workload_qkv(w))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.causal, w.scale, threads=1)
+        dt = time.perf_counter() - t0
+        pairs = w.B * w.H * (w.T * (w.T + 1) // 2 if w.causal else w.T * w.T)
+        flops = 4.0 * w.D * pairs
+        out.append({"workload": name, "seconds": dt, "flop": flops,
+                    "gflops": flops / dt / 1e9, "cores": 1})
+        log(f"oracle on one core, {name}: {dt:.3f} s, {flops / dt / 1e9:.2f} GFLOP/s")
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -686,6 +707,11 @@ def main():
         import oracle
         extra = contrast(osa, torch, oracle)
 
+    single = None
+    if not a.no_cpu_baseline:
+        import oracle
+        single = oracle_single_core(oracle)
+
     kname = osa.attn_kernel_name({"bf16": 0, "f16": 2, "f32": 4}[w.dtype] +
                                  (0 if w.causal else 1))
     line = {
@@ -712,6 +738,7 @@ def main():
         "kernels": kernels,
         "backward": bwd,
         "backward_atomic": bwd_atomic,
+        "cpu_single_core": single,
         "decode": dec,
         "head_dims": hds,
         "gated_recurrence": recur,
