@@ -130,12 +130,14 @@ def cpu_baseline(oracle, q, k, v, o, lse, w, nrows, seed):
     err_o = float(np.abs(got_o.astype(np.float64) - ro).max())
     err_l = float(np.abs(got_l.astype(np.float64) - rl).max())
     finite = bool(np.isfinite(got_o).all() and np.isfinite(got_l).all())
+    full = 2.0 * w.B * w.H * w.T * w.T * w.D * (1 if w.causal else 2)
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
         "sample": (f"{len(rows)} seeded rows (of {w.rows}) of {w.name}, all "
                    f"{w.D} dims, {flops:.3e} flop in {dt:.2f} s on {threads} "
                    f"threads of {cpu_model()}"),
+        "extrapolated_full_s": full / (flops / dt),
     }, {"rows": int(len(rows)), "max_abs_err_o": err_o,
         "max_abs_err_lse": err_l, "finite": finite}
 
