@@ -309,7 +309,7 @@ def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
     return out
 
 
-def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps=20,
+def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, D=64, dtype="bf16", steps=20,
                copies=4, with_oracle=True):
     """The decode path (attn_decode_stream): Tq new tokens per sequence
     against a Tk-token key/value cache, causal. It reads the cache once, so
@@ -322,17 +322,19 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps
     from online_softmax_amd.inputs import make_qkv
     dev = torch.device("cuda:0")
     scale = 0.125
-    (q,) = make_qkv(B, H, Tq, 64, dtype, 2101)[:1]
-    caches = [make_qkv(B, H, Tk, 64, dtype, 2102 + i)[1:] for i in range(copies)]
+    seed = 2101 if D == 64 else 2111
+    (q,) = make_qkv(B, H, Tq, D, dtype, seed)[:1]
+    caches = [make_qkv(B, H, Tk, D, dtype, seed + 1 + i)[1:] for i in range(copies)]
     qd = q.to(dev)
     kv = [(k.to(dev), v.to(dev)) for k, v in caches]
     o = torch.empty_like(qd)
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
-    ws = torch.empty(osa.attn_decode_workspace_bytes(B, H, Tq, Tk), dtype=torch.uint8,
+    ws = torch.empty(osa.attn_decode_workspace_bytes(B, H, Tq, Tk, D), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
-    out = {"workload": f"decode_b{B}h{H}_tq{Tq}_tk{Tk}_{dtype}", "B": B, "H": H,
-           "Tq": Tq, "Tk": Tk, "causal": True, "scale": scale,
+    dname = "" if D == 64 else f"_d{D}"
+    out = {"workload": f"decode_b{B}h{H}_tq{Tq}_tk{Tk}{dname}_{dtype}", "B": B, "H": H,
+           "Tq": Tq, "Tk": Tk, "D": D, "causal": True, "scale": scale,
            "kernels": ["decode_split16", "decode_combine16"]}
     osa.attn_decode_stream(qd, kv[0][0], kv[0][1], o, lse, ws, True, scale, stream)
     torch.cuda.synchronize()
@@ -347,7 +349,7 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps
         ok = eo <= BF16_TOL and el <= BF16_TOL and bool(torch.isfinite(o.float()).all())
         out["parity"] = {"rows": B * H * Tq, "max_abs_err_o": eo, "max_abs_err_lse": el,
                          "bound": BF16_TOL, "pass": ok}
-        kv_bytes = 2 * B * H * Tk * 64 * (4 if dtype == "f32" else 2)
+        kv_bytes = 2 * B * H * Tk * D * (4 if dtype == "f32" else 2)
         out["cpu_baseline"] = {
             "value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"every row of the decode workload in {dt:.2f} s on {threads} "
@@ -376,14 +378,14 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, dtype="bf16", steps
     # launch; the median is the call's duration, the mean is reported too
     med = statistics.median(ms)
     elt = 2
-    algo = 2 * B * H * Tk * 64 * elt + 2 * B * H * Tq * 64 * elt + 4 * B * H * Tq
+    algo = 2 * B * H * Tk * D * elt + 2 * B * H * Tq * D * elt + 4 * B * H * Tq
     achieved = algo / (med * 1e-3) / 1e9
     out.update({"ms": {"mean": mean, "median": statistics.median(ms), "min": min(ms)},
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                              "algorithmic_bytes_per_call": algo},
                 "pass": True})
-    log(f"decode: median {med * 1e3:.1f} us (mean {mean * 1e3:.1f}), {achieved:.0f} GB/s = "
+    log(f"decode D={D}: median {med * 1e3:.1f} us (mean {mean * 1e3:.1f}), {achieved:.0f} GB/s = "
         f"{100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s")
     del kv, qd, o, lse, ws
     return out
@@ -688,10 +690,12 @@ def main():
                                   cache=cache)
         bwd_atomic.pop("cpu_baseline", None)
 
-    dec = None
+    dec = dec128 = None
     if not a.no_decode:
         import oracle
         dec = decode_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
+        dec128 = decode_leg(osa, torch, oracle, D=128, with_oracle=not a.no_cpu_baseline)
+        dec128.pop("cpu_baseline", None)
 
     hds = None
     if not a.no_head_dims:
@@ -742,6 +746,7 @@ def main():
         "backward_atomic": bwd_atomic,
         "cpu_single_core": single,
         "decode": dec,
+        "decode_d128": dec128,
         "head_dims": hds,
         "gated_recurrence": recur,
         "contrast_fp32_single_head": extra,

@@ -199,26 +199,29 @@ size_t attn_bwd_atomic_workspace_bytes(int B, int H, int T);
  * o         : device, [B, H, Tq, D] of `dtype`, written.
  * lse       : device, float32 [B, H, Tq] (natural log), written; may be NULL.
  * workspace : caller-owned device buffer of at least
- *             attn_decode_workspace_bytes(B, H, Tq, Tk) bytes (16-byte
+ *             attn_decode_workspace_bytes(B, H, Tq, Tk, D) bytes (16-byte
  *             aligned) for the per-split partial results; contents undefined
  *             afterwards.
- * Tq, Tk    : 1 <= Tq <= Tk. D must be 64. scale, stream as attn_fwd_stream.
+ * Tq, Tk    : 1 <= Tq <= Tk. D is 32, 64 or 128. scale, stream as
+ *             attn_fwd_stream.
  * dtype     : ATTN_BF16 or ATTN_F16; ATTN_F32 returns ATTN_ERR_UNSUPPORTED.
  *
  * The keys are split over workgroups and the partial results merged with the
  * log-sum-exp identity O = sum_s exp(lse_s - lse) O_s. Returns ATTN_OK once
  * enqueued, or an error status with nothing enqueued (ATTN_ERR_INVALID for a
  * null or misaligned pointer, Tq > Tk, a bad size, dtype or scale, a short
- * workspace; ATTN_ERR_UNSUPPORTED for D != 64, float32, or sizes beyond one
- * launch or a 4 GiB slice).
+ * workspace; ATTN_ERR_UNSUPPORTED for another D, float32, or sizes beyond
+ * one launch or a 4 GiB slice).
  */
 int attn_decode_stream(const void* q, const void* k, const void* v, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, int B, int H, int Tq,
                        int Tk, int D, int causal, float scale, int dtype, void* stream);
 
 /* Workspace bytes attn_decode_stream needs for these sizes (the split is
- * chosen from them); 0 for invalid sizes or on overflow. */
-size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk);
+ * chosen from them): about B*H*Tq*nsplit*(D + 1)*4, nsplit the number of key
+ * ranges; 0 for invalid sizes, a head dimension other than 32, 64 or 128, or
+ * on overflow. */
+size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk, int D);
 
 /*
  * attn_gated_recurrence_stream - the gated linear recurrence of the

@@ -86,7 +86,7 @@ def load(path: str = LIBRARY):
         lib.attn_bwd_flops.argtypes = [I, I, I, I, I]
         lib.attn_bwd_flops.restype = ctypes.c_double
         lib.attn_decode_stream.argtypes = [P] * 6 + [S, I, I, I, I, I, I, F, I, P]
-        lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
+        lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
         lib.attn_decode_workspace_bytes.restype = S
         lib.attn_gated_recurrence_stream.argtypes = [P] * 5 + [I, I, I, I, P]
         lib.attn_gated_recurrence_flops.argtypes = [I, I, I, I]
@@ -263,8 +263,8 @@ def attn_bwd_atomic_stream(q, k, v, o, dout, lse, dq, dk, dv, workspace,
               workspace, causal, scale, stream)
 
 
-def attn_decode_workspace_bytes(B: int, H: int, Tq: int, Tk: int) -> int:
-    return int(_lib().attn_decode_workspace_bytes(B, H, Tq, Tk))
+def attn_decode_workspace_bytes(B: int, H: int, Tq: int, Tk: int, D: int = 64) -> int:
+    return int(_lib().attn_decode_workspace_bytes(B, H, Tq, Tk, D))
 
 
 def attn_decode_stream(q, k, v, o, lse, workspace, causal: bool, scale: float,
@@ -408,7 +408,7 @@ def attention_decode(q, k, v, causal: bool = True, scale: float | None = None,
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
-    ws = torch.empty(attn_decode_workspace_bytes(B, H, Tq, Tk), dtype=torch.uint8,
+    ws = torch.empty(attn_decode_workspace_bytes(B, H, Tq, Tk, D), dtype=torch.uint8,
                      device=q.device)
     attn_decode_stream(q, k, v, o, lse, ws, causal, scale, stream)
     return o, lse

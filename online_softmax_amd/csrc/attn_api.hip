@@ -35,8 +35,8 @@ bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
     return true;
 }
 
-// Head dimensions the 16-bit forward kernels are built for; every other
-// path (float32 forward, naive, backward, decode) takes 64 only.
+// Head dimensions the 16-bit forward and decode kernels are built for; every
+// other path (float32 forward, naive, backward) takes 64 only.
 bool fwd16_head_dim(int D) { return D == 32 || D == attn::kHeadDim || D == 128; }
 
 // Shape checks shared by every path, for a head dimension the caller
@@ -196,8 +196,8 @@ int attn_bwd_atomic_stream(const void* q, const void* k, const void* v, const vo
     return ATTN_OK;
 }
 
-size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk) {
-    if (B < 1 || H < 1 || Tq < 1 || Tk < Tq) return 0;
+size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk, int D) {
+    if (B < 1 || H < 1 || Tq < 1 || Tk < Tq || !fwd16_head_dim(D)) return 0;
     uint64_t bh, rows;
     if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || bh > (uint64_t)INT32_MAX) return 0;
     if (!mul_ok(bh, (uint64_t)Tq, &rows)) return 0;
@@ -205,7 +205,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk) {
     attn::decode_plan((int)bh, Tq, Tk, &nsplit, &chunk);
     uint64_t parts, bytes;
     if (!mul_ok(rows, (uint64_t)nsplit, &parts)) return 0;
-    if (!mul_ok(parts, (uint64_t)(attn::kHeadDim + 1) * 4, &bytes)) return 0;
+    if (!mul_ok(parts, (uint64_t)(D + 1) * 4, &bytes)) return 0;
     if (bytes > UINT64_MAX - 1024) return 0;
     return (size_t)((bytes + 256 + 255) & ~(uint64_t)255);
 }
@@ -216,7 +216,7 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
     if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID;
     if (B < 1 || H < 1 || Tq < 1 || Tk < 1 || D < 1) return ATTN_ERR_INVALID;
     if (Tq > Tk) return ATTN_ERR_INVALID;
-    int st = check_shape(B, H, Tk, D, D == attn::kHeadDim);
+    int st = check_shape(B, H, Tk, D, fwd16_head_dim(D));
     if (st != ATTN_OK) return st;
     if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
     if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -225,7 +225,7 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
         !aligned16(workspace))
         return ATTN_ERR_INVALID;
     if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
-    const size_t need = attn_decode_workspace_bytes(B, H, Tq, Tk);
+    const size_t need = attn_decode_workspace_bytes(B, H, Tq, Tk, D);
     if (need == 0) return ATTN_ERR_UNSUPPORTED;
     if (workspace_bytes < need) return ATTN_ERR_INVALID;
     if ((uint64_t)Tk * D * 2 > UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
@@ -240,8 +240,8 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
     if (!isfinite((float)c)) return ATTN_ERR_INVALID;
     const uint64_t parts = (uint64_t)BH * Tq * nsplit;
     float* o_part = (float*)workspace;
-    float* lse_part = o_part + parts * attn::kHeadDim;
-    const hipError_t e = attn::launch_decode(q, k, v, o, lse, o_part, lse_part, BH, Tq, Tk,
+    float* lse_part = o_part + parts * D;
+    const hipError_t e = attn::launch_decode(q, k, v, o, lse, o_part, lse_part, BH, Tq, Tk, D,
                                              causal ? 1 : 0, (float)c, scale < 0.0f, dtype,
                                              (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -401,7 +401,7 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
            attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels +
-           attn::kBwdAtomicKernels;
+           attn::kBwdAtomicKernels + attn::kDecodeHdKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -435,7 +435,13 @@ const char* attn_kernel_name(int kernel) {
         "bwd_prep16<bf16>",          "bwd_kvq16<bf16, causal>",
         "bwd_kvq16<bf16, full>",     "bwd_dq_finish16<bf16>",
         "bwd_prep16<f16>",           "bwd_kvq16<f16, causal>",
-        "bwd_kvq16<f16, full>",      "bwd_dq_finish16<f16>"};
+        "bwd_kvq16<f16, full>",      "bwd_dq_finish16<f16>",
+        "decode_split16<bf16, causal, 32>", "decode_split16<bf16, full, 32>",
+        "decode_combine16<bf16, 32>", "decode_split16<f16, causal, 32>",
+        "decode_split16<f16, full, 32>", "decode_combine16<f16, 32>",
+        "decode_split16<bf16, causal, 128>", "decode_split16<bf16, full, 128>",
+        "decode_combine16<bf16, 128>", "decode_split16<f16, causal, 128>",
+        "decode_split16<f16, full, 128>", "decode_combine16<f16, 128>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -447,13 +453,15 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     const int dec0 = bwd0 + attn::kBwdKernels, hd0 = dec0 + attn::kDecodeKernels;
     const int rec0 = hd0 + attn::kHdKernels;
     const int bat0 = rec0 + attn::kRecurrenceKernels;
+    const int dhd0 = bat0 + attn::kBwdAtomicKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
                      : kernel < hd0  ? attn::decode_kernel_ptr(kernel - dec0)
                      : kernel < rec0 ? attn::hd_kernel_ptr(kernel - hd0)
                      : kernel < bat0 ? attn::recurrence_kernel_ptr(kernel - rec0)
-                                     : attn::bwd_atomic_kernel_ptr(kernel - bat0);
+                     : kernel < dhd0 ? attn::bwd_atomic_kernel_ptr(kernel - bat0)
+                                     : attn::decode_kernel_ptr(6 + kernel - dhd0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);

@@ -33,34 +33,42 @@ namespace attn {
 
 constexpr float kDecLn2 = 0.693147180559945309417f;
 
-// One 32-key tile of K or V into `off` (4 wave instructions): rows from
-// row0, rows at or past `rows_end` fetch row rows_end - 1 (their weight is
-// masked to 0).
-__device__ inline void dec_load(v4u32_rsrc rs, const uint32_t (&voff)[4], int row0,
-                                int rows_end, uint32_t off) {
+// One 32-key tile of K or V (head dimension D) into `off` (D / 16 wave
+// instructions): rows from row0, rows at or past `rows_end` fetch row
+// rows_end - 1 (their weight is masked to 0).
+template <int D>
+__device__ inline void dec_load(v4u32_rsrc rs, const uint32_t (&voff)[dec_instr<D>()],
+                                int row0, int rows_end, uint32_t off) {
+    constexpr uint32_t kRow = HeadDim<D>::kRowBytes;
     if (row0 + kDecTile <= rows_end) {
-        const uint32_t soff = (uint32_t)row0 * (kHeadDim * 2);
+        const uint32_t soff = (uint32_t)row0 * kRow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(rs, voff[i], soff, off + 1024 * i);
+        for (int i = 0; i < dec_instr<D>(); ++i) dma16(rs, voff[i], soff, off + 1024 * i);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = min(row0 + (int)(voff[i] >> 7), rows_end - 1);
-            dma16(rs, (uint32_t)r * (kHeadDim * 2) + (voff[i] & 127), 0u, off + 1024 * i);
+        for (int i = 0; i < dec_instr<D>(); ++i) {
+            const int r = min(row0 + (int)(voff[i] / kRow), rows_end - 1);
+            dma16(rs, (uint32_t)r * kRow + voff[i] % kRow, 0u, off + 1024 * i);
         }
     }
 }
 
-// Partial results of one split: o_part [rows, nsplit, 64] float32 (normalised
+// Partial results of one split: o_part [rows, nsplit, D] float32 (normalised
 // by the split's own denominator), lse_part [rows, nsplit] (natural log; -inf
 // where the split holds no visible key of the row). rows = BH * Tq.
-template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void decode_split16(
+// At D = 128 the ring (128 KiB) leaves room for one workgroup per CU, which
+// is all the split plan launches.
+template <int DT, bool CAUSAL, int D>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
     int Tq, int Tk, int nqt, int nsplit, int chunk, float c, uint32_t qsign) {
+    using G = HeadDim<D>;
     constexpr int kStages = 2;
-    __shared__ __attribute__((aligned(1024))) char ring[kWaves][kStages][2][kDecTileBytes];
+    constexpr int NI = dec_instr<D>();     // direct loads per K or V tile
+    constexpr int NK = G::kSteps, NO = G::kOTiles;
+    constexpr int kTile = dec_tile_bytes<D>();
+    __shared__ __attribute__((aligned(1024))) char ring[kWaves][kStages][2][kTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -84,15 +92,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
     // this lane's first invisible key
     const int limit = min(k_end, CAUSAL ? (Tk - Tq + my_q + 1) : Tk);
 
-    const uint32_t slice_bytes = (uint32_t)Tk * (kHeadDim * 2);
-    const int64_t kv_base = (int64_t)bh * Tk * kHeadDim;
+    const uint32_t slice_bytes = (uint32_t)Tk * G::kRowBytes;
+    const int64_t kv_base = (int64_t)bh * Tk * D;
     const v4u32_rsrc krs = buffer_rsrc(k + kv_base, slice_bytes);
     const v4u32_rsrc vrs = buffer_rsrc(v + kv_base, slice_bytes);
-    uint32_t kvoff[4], vvoff[4];
+    uint32_t kvoff[NI], vvoff[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        kvoff[i] = (uint32_t)dl_global_byte(i >> 1, i & 1, lane, false);
-        vvoff[i] = (uint32_t)dl_global_byte(i >> 1, i & 1, lane, true);
+    for (int i = 0; i < NI; ++i) {
+        kvoff[i] = (uint32_t)G::global_byte(i, lane, false);
+        vvoff[i] = (uint32_t)G::global_byte(i, lane, true);
     }
     // this wave's tiles: k_begin + 32 * (wave + 4 t), t = 0 .. n - 1
     const int ntile_all = k_end > k_begin ? (k_end - k_begin + kDecTile - 1) / kDecTile : 0;
@@ -101,20 +109,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
     auto issue = [&](int t) {
         const int k0 = k_begin + kDecTile * (wave_u + kWaves * t);
         const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)ring[wave_u][t % kStages][0];
-        dec_load(krs, kvoff, k0, k_end, base);
-        dec_load(vrs, vvoff, k0, k_end, base + kDecTileBytes);
+        dec_load<D>(krs, kvoff, k0, k_end, base);
+        dec_load<D>(vrs, vvoff, k0, k_end, base + kTile);
     };
 
     // lane bases of the fragment reads (the swizzles depend on the lane only)
-    uint32_t ko[4], vo[2];
+    uint32_t ko[NK], vo[NO];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ko[ks] = (uint32_t)kfrag_byte(ql, hh, 0, ks);
+    for (int ks = 0; ks < NK; ++ks) ko[ks] = (uint32_t)G::kfrag(ql, hh, 0, ks);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) vo[mt] = (uint32_t)vtr_byte(lane, mt, 0, 0);
+    for (int mt = 0; mt < NO; ++mt) vo[mt] = (uint32_t)G::vtr(lane, mt, 0, 0);
 
-    v16f32 oacc[2];
+    v16f32 oacc[NO];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NO; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
     float m = -FLT_MAX, mc = -FLT_MAX * c, l = 0.f;
@@ -123,17 +131,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
     // compiler's wait for Q before its first use also covers the tiles)
     if (n >= 1) issue(0);
     if (n >= 2) issue(1);
-    v4u32 qf[4];
+    v4u32 qf[NK];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
         v4u32 x = {0u, 0u, 0u, 0u};
         if (my_q < Tq)
-            x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * kHeadDim + q_col16(hh, ks));
+            x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * D + G::q_col(hh, ks));
         qf[ks] = x ^ qsign;
     }
     for (int t = 0; t < n; ++t) {
         if (t + 1 < n)
-            wait_vmcnt<8>();  // tile t landed, tile t+1 (8 loads) in flight
+            wait_vmcnt<2 * NI>();  // tile t landed, tile t+1 (2 NI loads) in flight
         else
             wait_vmcnt<0>();
         const char* kb = ring[wave][t % kStages][0];
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < NK; ++ks)
             s = mfma16<DT>(*(const v4u32*)(kb + ko[ks]), qf[ks], s);
         // mask, running maximum, rescale
         float mx = -INFINITY;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
         mc = mc_new;
         l *= corr;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NO; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[mt][r] *= corr;
         // weights of the tile's 32 keys: P fragments of two 16-key steps
@@ -182,14 +190,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
         l += t0;
         // O^T += V^T P^T
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < NO; ++mt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-                const char* p = vb + vo[mt] + kVtrKsStride * ks;
+                const char* p = vb + vo[mt] + 16 * G::kRowBytes * ks;
                 const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-                const v4i16 b =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + kVtrHalfStride));
+                const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(p + 8 * G::kRowBytes));
                 const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
                 oacc[mt] = mfma16<DT>((v4u32){a2[0], a2[1], b2[0], b2[1]}, pf[ks], oacc[mt]);
             }
@@ -199,29 +207,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
 
     // merge the four waves' states through LDS (the ring is free now)
     __syncthreads();
-    float* so = (float*)&ring[0][0][0][0];      // [wave][32 queries][64 dims]
-    float* sm = so + kWaves * kDecTile * kHeadDim;  // [wave][32] reference mc
-    float* sl = sm + kWaves * kDecTile;             // [wave][32] denominator
+    float* so = (float*)&ring[0][0][0][0];  // [wave][32 queries][D dims]
+    float* sm = so + kWaves * kDecTile * D;  // [wave][32] reference mc
+    float* sl = sm + kWaves * kDecTile;      // [wave][32] denominator
     const float lt = halves_sum(l);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NO; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            so[(wave * kDecTile + ql) * kHeadDim + 32 * mt + acc_row(r, hh)] = oacc[mt][r];
+            so[(wave * kDecTile + ql) * D + 32 * mt + acc_row(r, hh)] = oacc[mt][r];
     if (hh == 0) {
         sm[wave * kDecTile + ql] = mc;
         sl[wave * kDecTile + ql] = lt;
     }
     __syncthreads();
-    // thread -> (query row, 8 dims)
-    const int rq = tid >> 3, d0 = 8 * (tid & 7);
+    // thread -> (query row, D / 8 dims)
+    constexpr int kDims = D / 8;
+    const int rq = tid >> 3, d0 = kDims * (tid & 7);
     const int qrow = qt * kDecTile + rq;
     if (qrow < Tq) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
             if (sl[w * kDecTile + rq] > 0.f) M = fmaxf(M, sm[w * kDecTile + rq]);
-        float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float L = 0.f, acc[kDims];
+#pragma unroll
+        for (int j = 0; j < kDims; ++j) acc[j] = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
@@ -230,13 +241,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split16(
                 const float e = fast_exp2(sm[w * kDecTile + rq] - M);
                 L += e * lw;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] += e * so[(w * kDecTile + rq) * kHeadDim + d0 + j];
+                for (int j = 0; j < kDims; ++j) acc[j] += e * so[(w * kDecTile + rq) * D + d0 + j];
             }
         }
         const int64_t p = ((int64_t)bh * Tq + qrow) * nsplit + split;
         const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o_part[p * kHeadDim + d0 + j] = acc[j] * inv;
+        for (int j = 0; j < kDims; ++j) o_part[p * D + d0 + j] = acc[j] * inv;
         if ((tid & 7) == 0) lse_part[p] = L > 0.f ? (M + log2f(L)) * kDecLn2 : -INFINITY;
     }
 }
@@ -256,21 +267,27 @@ __device__ inline float wave_sum(float x) {
     return x;
 }
 
-template <int DT>
+// Lane j holds dims j, j + 64, ... below D (lanes 32..63 of a D = 32 row
+// repeat lanes 0..31 and store nothing).
+template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_combine16(const float* __restrict__ o_part,
                                                         const float* __restrict__ lse_part,
                                                         uint16_t* __restrict__ o,
                                                         float* __restrict__ lse, int64_t rows,
                                                         int nsplit) {
+    constexpr int NPL = D >= 64 ? D / 64 : 1;  // dims per lane
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
+    const int dim = D >= 64 ? lane : (lane & (D - 1));
     const float* lp = lse_part + row * nsplit;
-    const float* op = o_part + row * nsplit * kHeadDim + lane;
+    const float* op = o_part + row * nsplit * D + dim;
     float M = -INFINITY;
     for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, lp[s]);
     M = wave_max(M);
-    float L = 0.f, acc = 0.f;
+    float L = 0.f, acc[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += 64) {
         const int s = s0 + lane;
         const float ls = s < nsplit ? lp[s] : -INFINITY;
@@ -280,16 +297,32 @@ __global__ __launch_bounds__(256) void decode_combine16(const float* __restrict_
         const uint32_t eb = __builtin_bit_cast(uint32_t, e);
         for (int j = 0; j < cnt; ++j) {
             const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
-            acc += ej * op[(int64_t)(s0 + j) * kHeadDim];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) acc[i] += ej * op[(int64_t)(s0 + j) * D + 64 * i];
         }
     }
-    const float val = acc / L;
-    o[row * kHeadDim + lane] = (uint16_t)(pack2<DT>(val, 0.f) & 0xffffu);
+    if (D >= 64 || lane < D) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            o[row * D + dim + 64 * i] = (uint16_t)(pack2<DT>(acc[i] / L, 0.f) & 0xffffu);
+    }
     if (lane == 0 && lse != nullptr) lse[row] = M + logf(L);
 }
 
+template <int DT, int D>
+void launch_decode_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                     float* lse, float* o_part, float* lse_part, int Tq, int Tk, int nqt,
+                     int nsplit, int chunk, int causal, float c, uint32_t sign, dim3 grid,
+                     dim3 cgrid, int64_t rows, hipStream_t stream) {
+    auto fn = causal ? decode_split16<DT, true, D> : decode_split16<DT, false, D>;
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q, k, v, o_part, lse_part, Tq, Tk,
+                       nqt, nsplit, chunk, c, sign);
+    hipLaunchKernelGGL((decode_combine16<DT, D>), cgrid, dim3(256), 0, stream, o_part,
+                       lse_part, o, lse, rows, nsplit);
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                         float* o_part, float* lse_part, int BH, int Tq, int Tk,
+                         float* o_part, float* lse_part, int BH, int Tq, int Tk, int D,
                          int causal, float c, bool negate_q, int dt, hipStream_t stream) {
     int nsplit, chunk;
     decode_plan(BH, Tq, Tk, &nsplit, &chunk);
@@ -301,32 +334,44 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
     const uint16_t* q16 = (const uint16_t*)q;
     const uint16_t* k16 = (const uint16_t*)k;
     const uint16_t* v16 = (const uint16_t*)v;
-    if (dt == ATTN_DT_BF16) {
-        auto fn = causal ? decode_split16<ATTN_DT_BF16, true> : decode_split16<ATTN_DT_BF16, false>;
-        hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q16, k16, v16, o_part,
-                           lse_part, Tq, Tk, nqt, nsplit, chunk, c, sign);
-        hipLaunchKernelGGL(decode_combine16<ATTN_DT_BF16>, cgrid, dim3(256), 0, stream,
-                           o_part, lse_part, (uint16_t*)o, lse, rows, nsplit);
-    } else {
-        auto fn = causal ? decode_split16<ATTN_DT_F16, true> : decode_split16<ATTN_DT_F16, false>;
-        hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q16, k16, v16, o_part,
-                           lse_part, Tq, Tk, nqt, nsplit, chunk, c, sign);
-        hipLaunchKernelGGL(decode_combine16<ATTN_DT_F16>, cgrid, dim3(256), 0, stream,
-                           o_part, lse_part, (uint16_t*)o, lse, rows, nsplit);
+    uint16_t* o16 = (uint16_t*)o;
+#define ATTN_DECODE_CASE(DTV, DV)                                                           \
+    if (dt == DTV && D == DV) {                                                             \
+        launch_decode_d<DTV, DV>(q16, k16, v16, o16, lse, o_part, lse_part, Tq, Tk, nqt,   \
+                                 nsplit, chunk, causal, c, sign, grid, cgrid, rows, stream); \
+        return hipGetLastError();                                                           \
     }
-    return hipGetLastError();
+    ATTN_DECODE_CASE(ATTN_DT_BF16, 64)
+    ATTN_DECODE_CASE(ATTN_DT_F16, 64)
+    ATTN_DECODE_CASE(ATTN_DT_BF16, 32)
+    ATTN_DECODE_CASE(ATTN_DT_F16, 32)
+    ATTN_DECODE_CASE(ATTN_DT_BF16, 128)
+    ATTN_DECODE_CASE(ATTN_DT_F16, 128)
+#undef ATTN_DECODE_CASE
+    return hipErrorInvalidValue;
+}
+
+// Kernels 0..5 are the D = 64 ones, then D = 32 (6..11) and D = 128 (12..17),
+// each group ordered bf16 {causal, full, combine}, f16 {causal, full, combine}.
+template <int D>
+static const void* decode_group_ptr(int index) {
+    switch (index) {
+        case 0: return (const void*)decode_split16<ATTN_DT_BF16, true, D>;
+        case 1: return (const void*)decode_split16<ATTN_DT_BF16, false, D>;
+        case 2: return (const void*)decode_combine16<ATTN_DT_BF16, D>;
+        case 3: return (const void*)decode_split16<ATTN_DT_F16, true, D>;
+        case 4: return (const void*)decode_split16<ATTN_DT_F16, false, D>;
+        case 5: return (const void*)decode_combine16<ATTN_DT_F16, D>;
+        default: return nullptr;
+    }
 }
 
 const void* decode_kernel_ptr(int index) {
-    switch (index) {
-        case 0: return (const void*)decode_split16<ATTN_DT_BF16, true>;
-        case 1: return (const void*)decode_split16<ATTN_DT_BF16, false>;
-        case 2: return (const void*)decode_combine16<ATTN_DT_BF16>;
-        case 3: return (const void*)decode_split16<ATTN_DT_F16, true>;
-        case 4: return (const void*)decode_split16<ATTN_DT_F16, false>;
-        case 5: return (const void*)decode_combine16<ATTN_DT_F16>;
-        default: return nullptr;
-    }
+    if (index < 0) return nullptr;
+    if (index < 6) return decode_group_ptr<64>(index);
+    if (index < 12) return decode_group_ptr<32>(index - 6);
+    if (index < 18) return decode_group_ptr<128>(index - 12);
+    return nullptr;
 }
 
 }  // namespace attn

@@ -195,9 +195,13 @@ ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
 //     transposed read land in distinct quarters of the row);
 //   D = 32 (4 chunks, 4 rows per 256 bytes): K chunk c at c ^ ((r >> 2) & 3);
 //     V needs none (a transposed read's 4 rows x 4 chunks are 256 whole
-//     bytes).
+//     bytes);
+//   D = 64: swz_k and swz_v above, so that HeadDim<64> addresses the tiles
+//     of the D = 64 kernels byte for byte (the decode kernels take every
+//     head dimension through this struct).
 template <int D>
 struct HeadDim {
+    static_assert(D == 32 || D == 64 || D == 128, "head dimension without a layout");
     static constexpr int kChunks = D / 8;
     static constexpr int kRowBytes = 2 * D;
     static constexpr int kTileBytes = 64 * kRowBytes;
@@ -205,8 +209,12 @@ struct HeadDim {
     static constexpr int kInstrPerWave = kInstr / kWaves;
     static constexpr int kSteps = D / 16;                  // MFMA reduction steps of S
     static constexpr int kOTiles = D / 32;                 // 32-dim tiles of O
-    ATTN_HD static int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 2) & 3); }
-    ATTN_HD static int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 0; }
+    ATTN_HD static int swz_k(int r) {
+        return D == 128 ? (r & 15) : D == 64 ? attn::swz_k(r) : ((r >> 2) & 3);
+    }
+    ATTN_HD static int swz_v(int r) {
+        return D == 128 ? 4 * (r & 3) : D == 64 ? attn::swz_v(r) : 0;
+    }
     ATTN_HD static int k_byte(int row, int chunk) {
         return row * kRowBytes + ((chunk ^ swz_k(row)) << 4);
     }
@@ -361,7 +369,13 @@ ATTN_HD bool bwd_q_edge(int qt, int w, int u, int T, bool causal) {
 // (measured at 4 x 12 heads, one query, 8192 keys: 240 workgroups 27.6 us,
 // 480 29.1 us, 288 33.0 us).
 constexpr int kDecTile = 32;                             // keys per tile, queries per tile
-constexpr int kDecTileBytes = kDecTile * kHeadDim * 2;   // 4 KiB
+constexpr int kDecTileBytes = kDecTile * kHeadDim * 2;   // 4 KiB at D = 64
+// A 32-key tile of head dimension D is the first half of HeadDim<D>'s
+// 64-key tile: same swizzles, D / 16 direct-load wave instructions.
+template <int D>
+constexpr int dec_tile_bytes() { return kDecTile * HeadDim<D>::kRowBytes; }
+template <int D>
+constexpr int dec_instr() { return dec_tile_bytes<D>() / 1024; }
 ATTN_HD void decode_plan(int BH, int Tq, int Tk, int* nsplit, int* chunk) {
     const int nqt = (Tq + kDecTile - 1) / kDecTile;
     const long long base = (long long)BH * nqt;

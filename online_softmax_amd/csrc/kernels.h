@@ -40,11 +40,12 @@ hipError_t launch_bwd_atomic(const void* q, const void* k, const void* v, const 
                              float* delta, float* dq_acc, int BH, int T, int causal, float c,
                              float scale, bool negate, int dt, hipStream_t stream);
 
-// Decode: Tq queries against a Tk-token cache, split over the keys into
-// o_part [BH*Tq, nsplit, 64] and lse_part [BH*Tq, nsplit] (float32), then
-// merged; the split is decode_plan (fused_layout.h).
+// Decode: Tq queries against a Tk-token cache (head dimension D = 32, 64 or
+// 128), split over the keys into o_part [BH*Tq, nsplit, D] and lse_part
+// [BH*Tq, nsplit] (float32), then merged; the split is decode_plan
+// (fused_layout.h).
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                         float* o_part, float* lse_part, int BH, int Tq, int Tk,
+                         float* o_part, float* lse_part, int BH, int Tq, int Tk, int D,
                          int causal, float c, bool negate_q, int dt, hipStream_t stream);
 
 // Fused forward for head dimensions 32 and 128 (16-bit dtypes only).
@@ -64,10 +65,11 @@ constexpr int kDecodeKernels = 6;
 constexpr int kHdKernels = 8;
 constexpr int kRecurrenceKernels = 16;
 constexpr int kBwdAtomicKernels = 8;
+constexpr int kDecodeHdKernels = 12;  // decode at D = 32 and 128 (decode_kernel_ptr 6 .. 17)
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
-const void* decode_kernel_ptr(int index);
+const void* decode_kernel_ptr(int index);  // 0 .. 5 at D = 64, then D = 32, 128
 const void* hd_kernel_ptr(int index);
 const void* recurrence_kernel_ptr(int index);
 const void* bwd_atomic_kernel_ptr(int index);

@@ -448,16 +448,43 @@ static void check_bwd_access(int BH, int T, bool causal) {
 // The decode kernels: every workgroup's key range, each wave's tile loads
 // (rows clamped below the range end, inside the slice), the LDS ring and the
 // merge area, and the partial-result indices.
+template <int D>
 static void check_decode(int BH, int Tq, int Tk, bool causal) {
+    using G = HeadDim<D>;
+    constexpr int kTile = dec_tile_bytes<D>();
+    constexpr long kRow = G::kRowBytes;
     int nsplit, chunk;
     decode_plan(BH, Tq, Tk, &nsplit, &chunk);
     CHECK(nsplit >= 1 && chunk % (kWaves * kDecTile) == 0, "decode plan");
     CHECK((long)nsplit * chunk >= Tk && (long)(nsplit - 1) * chunk < Tk, "decode split cover");
     const int nqt = (Tq + kDecTile - 1) / kDecTile;
     const long parts = (long)BH * Tq * nsplit;
-    const long ring_bytes = (long)kWaves * 2 * 2 * kDecTileBytes;
-    CHECK((long)kWaves * kDecTile * kHeadDim * 4 + 2 * kWaves * kDecTile * 4 <= ring_bytes,
+    const long ring_bytes = (long)kWaves * 2 * 2 * kTile;
+    CHECK(ring_bytes <= 160 * 1024, "decode ring exceeds the LDS");
+    CHECK(kTile == 1024 * dec_instr<D>() && 2 * dec_instr<D>() <= 63, "decode tile loads");
+    CHECK((long)kWaves * kDecTile * D * 4 + 2 * kWaves * kDecTile * 4 <= ring_bytes,
           "decode merge area exceeds the ring");
+    // the merge's threads (query row, D / 8 dims) cover each row once
+    {
+        std::vector<int> mcov(kDecTile * D, 0);
+        for (int tid = 0; tid < kThreads; ++tid)
+            for (int j = 0; j < D / 8; ++j) mcov[(tid >> 3) * D + (D / 8) * (tid & 7) + j]++;
+        for (int x = 0; x < kDecTile * D; ++x) CHECK(mcov[x] == 1, "decode merge cover");
+    }
+    // the combine's lanes cover each of a row's D dims once
+    {
+        const int npl = D >= 64 ? D / 64 : 1;
+        std::vector<int> ccov(D, 0);
+        for (int lane = 0; lane < 64; ++lane) {
+            if (!(D >= 64 || lane < D)) continue;
+            const int dim = D >= 64 ? lane : (lane & (D - 1));
+            for (int i = 0; i < npl; ++i) {
+                CHECK(dim + 64 * i < D, "decode combine dim");
+                ccov[dim + 64 * i]++;
+            }
+        }
+        for (int x = 0; x < D; ++x) CHECK(ccov[x] == 1, "decode combine cover");
+    }
     std::vector<int> covered((size_t)Tk, 0);
     for (int b = 0; b < BH * nqt * nsplit; ++b) {
         const int per = nqt * nsplit, bh = b / per, rem = b % per;
@@ -475,20 +502,21 @@ static void check_decode(int BH, int Tq, int Tk, bool causal) {
                 CHECK(k0 < k_end, "decode tile past the range");
                 if (bh == 0 && qt == nqt - 1)
                     for (int r = 0; r < kDecTile && k0 + r < k_end; ++r) covered[k0 + r]++;
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < dec_instr<D>(); ++i)
                     for (int l = 0; l < 64; ++l)
                         for (int is_v = 0; is_v < 2; ++is_v) {
-                            const long voff = dl_global_byte(i >> 1, i & 1, l, is_v);
+                            const long voff = G::global_byte(i, l, is_v);
+                            CHECK(voff / kRow < kDecTile, "decode load row beyond the tile");
                             long off;
                             if (k0 + kDecTile <= k_end) {
-                                off = (long)k0 * 128 + voff;
+                                off = (long)k0 * kRow + voff;
                             } else {
-                                long r = k0 + (voff >> 7);
+                                long r = k0 + voff / kRow;
                                 if (r > k_end - 1) r = k_end - 1;
-                                off = r * 128 + (voff & 127);
+                                off = r * kRow + voff % kRow;
                             }
-                            CHECK(off >= 0 && off + 16 <= (long)Tk * 128, "decode load outside slice");
-                            CHECK(1024 * i + 16 * l + 16 <= kDecTileBytes, "decode LDS tile");
+                            CHECK(off >= 0 && off + 16 <= (long)Tk * kRow, "decode load outside slice");
+                            CHECK(1024 * i + 16 * l + 16 <= kTile, "decode LDS tile");
                         }
             }
         }
@@ -502,6 +530,60 @@ static void check_decode(int BH, int Tq, int Tk, bool causal) {
     // the last query tile of a slice sees every key its queries may see, once
     const int kend_last = causal ? Tk : Tk;
     for (int j = 0; j < kend_last; ++j) CHECK(covered[j] == 1, "decode key %d covered %d times", j, covered[j]);
+}
+
+// The decode kernels read a 32-key tile of HeadDim<D>'s layout: the K
+// fragments (tile nt = 0) and the V^T reads (steps 0, 1) stay in its rows,
+// and the direct loads of its D / 16 instructions fill exactly those rows.
+template <int D>
+static void check_decode_tile() {
+    using G = HeadDim<D>;
+    constexpr int kTile = dec_tile_bytes<D>();
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        std::vector<int> cov(kDecTile * G::kChunks, 0);
+        for (int i = 0; i < dec_instr<D>(); ++i)
+            for (int l = 0; l < 64; ++l) {
+                int row, chunk;
+                G::src(i, l, is_v, &row, &chunk);
+                CHECK(row < kDecTile, "D%d decode load row", D);
+                cov[row * G::kChunks + chunk]++;
+            }
+        for (int x = 0; x < kDecTile * G::kChunks; ++x) CHECK(cov[x] == 1, "D%d decode cover", D);
+    }
+    for (int l = 0; l < 64; ++l) {
+        for (int ks = 0; ks < G::kSteps; ++ks)
+            CHECK(G::kfrag(l & 31, l >> 5, 0, ks) + 16 <= kTile, "D%d decode kfrag", D);
+        for (int mt = 0; mt < G::kOTiles; ++mt)
+            for (int ks = 0; ks < 2; ++ks)
+                for (int half = 0; half < 2; ++half)
+                    CHECK(G::vtr(l, mt, ks, half) + 8 <= kTile, "D%d decode vtr", D);
+    }
+}
+
+// HeadDim<64> is the D = 64 kernels' layout byte for byte.
+static void check_head_dim64_same() {
+    using G = HeadDim<64>;
+    for (int r = 0; r < 64; ++r) {
+        for (int c = 0; c < 8; ++c) CHECK(G::k_byte(r, c) == k_byte(r, c), "HeadDim<64> k_byte");
+        for (int d = 0; d < 64; ++d) CHECK(G::v_byte(r, d) == v_byte(r, d), "HeadDim<64> v_byte");
+    }
+    for (int l = 0; l < 64; ++l) {
+        for (int i = 0; i < 8; ++i)
+            for (int is_v = 0; is_v < 2; ++is_v)
+                CHECK(G::global_byte(i, l, is_v) == dl_global_byte(i >> 1, i & 1, l, is_v),
+                      "HeadDim<64> direct load");
+        for (int nt = 0; nt < 2; ++nt)
+            for (int ks = 0; ks < 4; ++ks)
+                CHECK(G::kfrag(l & 31, l >> 5, nt, ks) == kfrag_byte(l & 31, l >> 5, nt, ks),
+                      "HeadDim<64> kfrag");
+        for (int mt = 0; mt < 2; ++mt)
+            for (int ks = 0; ks < 4; ++ks)
+                for (int half = 0; half < 2; ++half)
+                    CHECK(G::vtr(l, mt, ks, half) == vtr_byte(l, mt, ks, half), "HeadDim<64> vtr");
+        for (int h = 0; h < 2; ++h)
+            for (int ks = 0; ks < 4; ++ks) CHECK(G::q_col(h, ks) == q_col16(h, ks), "HeadDim<64> q_col");
+    }
+    CHECK(dec_tile_bytes<64>() == kDecTileBytes, "decode tile bytes at D = 64");
 }
 
 // The pipelined dK/dV kernel masks only the wave's first tile and the last
@@ -860,12 +942,21 @@ int main() {
     for (int T = 1; T <= 700; T += (T < 300 ? 1 : 23))
         for (int causal = 0; causal < 2; ++causal) check_bwd_atomic_rows(T, causal);
     check_head_dim<32>();
+    check_head_dim<64>();
     check_head_dim<128>();
+    check_head_dim64_same();
+    check_decode_tile<32>();
+    check_decode_tile<64>();
+    check_decode_tile<128>();
     for (int Tk : {1, 2, 31, 32, 33, 127, 128, 129, 300, 1000, 4096, 8192})
         for (int Tq : {1, 2, 7, 31, 32, 33, 64, 100})
             for (int BH : {1, 6, 48})
                 for (int causal = 0; causal < 2; ++causal)
-                    if (Tq <= Tk) check_decode(BH, Tq, Tk, causal);
+                    if (Tq <= Tk) {
+                        check_decode<32>(BH, Tq, Tk, causal);
+                        check_decode<64>(BH, Tq, Tk, causal);
+                        check_decode<128>(BH, Tq, Tk, causal);
+                    }
     for (int T : {1, 63, 64, 65, 127, 128, 129, 300, 1000, 8192})
         for (int BH : {1, 6, 48})
             for (int causal = 0; causal < 2; ++causal) {

@@ -145,8 +145,8 @@ def dec(lib, q=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40, B=1, H=1, Tq=1, Tk=8,
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(ws=None), -1), (dict(Tq=0), -1), (dict(Tk=0), -1),
-    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=128), -2), (dict(D=32), -2),
-    (dict(dtype=0), -2),
+    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=96), -2), (dict(D=16), -2),
+    (dict(D=256), -2), (dict(dtype=0), -2),
     (dict(dtype=9), -1), (dict(scale=math.inf), -1), (dict(q=FAKE + 8), -1),
     (dict(ws=FAKE + 4), -1), (dict(lse=FAKE + 2), -1), (dict(ws_bytes=16), -1),
     (dict(Tk=1 << 25), -2),  # one cache slice over 4 GiB
@@ -177,12 +177,19 @@ def test_recurrence_flops():
 
 def test_decode_workspace_bytes():
     for B, H, Tq, Tk in [(1, 1, 1, 1), (4, 12, 1, 8192), (2, 3, 33, 1000)]:
-        n = osa.attn_decode_workspace_bytes(B, H, Tq, Tk)
-        assert n > 0 and n % 256 == 0
-        # at least one partial (64 floats + lse) per row
-        assert n >= B * H * Tq * 65 * 4
+        sizes = {}
+        for D in (32, 64, 128):
+            n = osa.attn_decode_workspace_bytes(B, H, Tq, Tk, D)
+            assert n > 0 and n % 256 == 0
+            # at least one partial (D floats + lse) per row
+            assert n >= B * H * Tq * (D + 1) * 4
+            sizes[D] = n
+        assert sizes[32] <= sizes[64] <= sizes[128]
+        assert osa.attn_decode_workspace_bytes(B, H, Tq, Tk) == sizes[64]
     assert osa.attn_decode_workspace_bytes(1, 1, 5, 4) == 0
     assert osa.attn_decode_workspace_bytes(0, 1, 1, 1) == 0
+    for D in (16, 48, 96, 256):
+        assert osa.attn_decode_workspace_bytes(1, 1, 1, 8, D) == 0
 
 
 def test_naive_workspace_bytes():
@@ -287,7 +294,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 59
+    assert n == 71
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None

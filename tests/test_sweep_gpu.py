@@ -1,7 +1,7 @@
 """A seeded sweep of random small shapes through every entry point, each
 against the double oracle with the bound its own tests use: the forward
 (every dtype; head dims 32, 64, 128 for 16-bit), both backward entry
-points, decode, and the gated recurrence. The shapes are drawn once from a
+points, decode (head dims 32, 64, 128), and the gated recurrence. The shapes are drawn once from a
 fixed seed, so a failure names a reproducible case; they mix lengths on and
 off the tile sizes (32, 64, 128) with batch and head counts that change the
 grid's shape (and, for float32, which of its two kernels runs).
@@ -39,9 +39,10 @@ FWD_CASES = [(dt, D, *c) for dt, D in (("f32", 64), ("bf16", 64), ("f16", 64),
              for c in _draw(4, 700)]
 BWD_CASES = [(dt, atomic, *c) for dt in ("bf16", "f16") for atomic in (False, True)
              for c in _draw(3, 400)]
-DEC_CASES = [(dt, *c) for dt in ("bf16", "f16") for c in _draw(4, 900)]
+DEC_CASES = [(dt, 64, *c) for dt in ("bf16", "f16") for c in _draw(4, 900)]
 REC_CASES = [(int(_rng.integers(1, 3)), int(_rng.integers(1, 200)),
               int(_rng.integers(1, 5)), int(_rng.integers(1, 65))) for _ in range(6)]
+DEC_HD_CASES = [(dt, D, *c) for dt, D in (("bf16", 128), ("f16", 32)) for c in _draw(3, 900)]
 
 
 def _max_err(got, want):
@@ -77,12 +78,12 @@ def test_sweep_backward(gpu_lib, dtype, atomic, B, H, T, causal, scale):
         assert _max_err(g.float().cpu().numpy(), w) <= 2e-2 * max(1.0, float(np.abs(w).max()))
 
 
-@pytest.mark.parametrize("dtype,B,H,Tk,causal,scale", DEC_CASES)
-def test_sweep_decode(gpu_lib, dtype, B, H, Tk, causal, scale):
+@pytest.mark.parametrize("dtype,D,B,H,Tk,causal,scale", DEC_CASES + DEC_HD_CASES)
+def test_sweep_decode(gpu_lib, dtype, D, B, H, Tk, causal, scale):
     Tq = int(1 + (Tk * 7919) % min(Tk, 40))  # 1 .. min(Tk, 40), from the case itself
-    (q,) = make_qkv(B, H, Tq, 64, dtype, 9300 + Tk)[:1]
-    _, k, v = make_qkv(B, H, Tk, 64, dtype, 9400 + Tk)
-    flush_print(f"[gpu] sweep decode {dtype} {B}x{H} Tq={Tq} Tk={Tk} causal={causal} "
+    (q,) = make_qkv(B, H, Tq, D, dtype, 9300 + Tk)[:1]
+    _, k, v = make_qkv(B, H, Tk, D, dtype, 9400 + Tk)
+    flush_print(f"[gpu] sweep decode {dtype} D={D} {B}x{H} Tq={Tq} Tk={Tk} causal={causal} "
                 f"scale={scale}")
     o, lse = gpu_lib.attention_decode(q.to(DEV), k.to(DEV), v.to(DEV), causal, scale)
     torch.cuda.synchronize()
