@@ -74,6 +74,24 @@ __device__ inline void pv_hd(const char* __restrict__ vb, const uint32_t (&vo)[D
         }
 }
 
+// Which head dimensions run the skewed loop (below): at D = 128 the 16
+// products of a tile's P.V take about as long as its weights, so the two
+// overlap; the third V stage fits two workgroups per CU (80 KiB each).
+template <int D>
+constexpr bool hd_skewed() { return D == 128; }
+
+// Schedule of the skewed loop's unmasked step: the previous tile's P.V
+// matrix instructions spread between the weights' vector instructions.
+template <int NO>
+__device__ inline void hd_sched_skewed() {
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+#pragma unroll
+    for (int i = 0; i < 4 * NO; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 96 / (4 * NO), 0);    // VALU
+    }
+}
+
 // One workgroup: query tile qt (128 rows) of slice bh. c = |scale| log2(e);
 // qsign negates Q for a negative scale.
 template <int DT, bool CAUSAL, int D>
@@ -84,8 +102,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_hd16(
     using G = HeadDim<D>;
     constexpr int BN = 64;
     constexpr int NK = G::kSteps, NO = G::kOTiles, NI = G::kInstrPerWave;
+    constexpr bool SKEW = hd_skewed<D>();
+    constexpr int kVStages = SKEW ? 3 : 2;
     __shared__ __attribute__((aligned(1024))) char kbuf[2][G::kTileBytes];
-    __shared__ __attribute__((aligned(1024))) char vbuf[2][G::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char vbuf[kVStages][G::kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -134,9 +154,10 @@ __global__ __launch_bounds__(kThreads, 2) void fused_hd16(
             }
         }
     };
+    // K tile t goes to stage t % 2, V tile t to stage t % kVStages
     auto issue = [&](int t) {
         load_tile(krs, kbuf[t & 1], kvoff, t);
-        load_tile(vrs, vbuf[t & 1], vvoff, t);
+        load_tile(vrs, vbuf[t % kVStages], vvoff, t);
     };
     if (n_tiles > 0) issue(0);
 
@@ -160,21 +181,58 @@ __global__ __launch_bounds__(kThreads, 2) void fused_hd16(
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
     RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
 
+    // Plain order: iteration t waits for tile t, then S, weights and P.V of
+    // tile t. Skewed order: iteration t waits only for K(t) (V(t), issued
+    // after it, may still be in flight; loads complete in order, so V(t-1)
+    // has landed), computes S(t), and makes tile t's weights while tile
+    // t-1's P.V products run on the matrix cores; the last tile's product
+    // follows the loop. K(t+1) then overwrites K(t-1), read in iteration
+    // t-1; V(t+1) overwrites V(t-2), read in iteration t-1.
+    v4u32 pprev[4];
+    bool has_prev = false;  // wave-uniform: a P of an earlier tile awaits its product
+    int vprev = 0;          // its V stage
+    auto flush = [&]() {
+        if (has_prev) pv_hd<DT, D>(vbuf[vprev], vo, pprev, oacc);
+        has_prev = false;
+    };
     auto step = [&](int t, auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
-        wait_vmcnt<0>();   // this wave's loads of tile t landed
-        __syncthreads();   // everyone's landed; tile t-1's buffers are free
+        if (SKEW)
+            wait_vmcnt<NI>();  // this wave's K(t) (and V(t-1)) landed
+        else
+            wait_vmcnt<0>();   // this wave's loads of tile t landed
+        __syncthreads();       // everyone's landed; the stages reloaded next are free
         if (t + 1 < n_tiles) issue(t + 1);
-        if (EDGE && CAUSAL && t * BN > wq0 + 31) return;  // no key visible
+        if (EDGE && CAUSAL && t * BN > wq0 + 31) {  // no key visible
+            if (SKEW) flush();
+            return;
+        }
         v16f32 s[2];
         v4u32 pf[4];
         qk_hd<DT, D>(kbuf[t & 1], ko, qf, s);
-        softmax_tile<DT, CAUSAL, EDGE, NO>(s, pf, oacc, st, c, t * BN, T, my_q, hh);
-        pv_hd<DT, D>(vbuf[t & 1], vo, pf, oacc);
+        if (SKEW) {
+            auto pending = [&]() {
+                flush();
+                if (!EDGE) hd_sched_skewed<NO>();
+            };
+            softmax_tile<DT, CAUSAL, EDGE, NO>(s, pf, oacc, st, c, t * BN, T, my_q, hh, pending);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pprev[i] = pf[i];
+            has_prev = true;
+            vprev = t % kVStages;
+        } else {
+            softmax_tile<DT, CAUSAL, EDGE, NO>(s, pf, oacc, st, c, t * BN, T, my_q, hh);
+            pv_hd<DT, D>(vbuf[t & 1], vo, pf, oacc);
+        }
     };
     int t = 0;
     for (; t < n_main; ++t) step(t, std::integral_constant<bool, false>());
     for (; t < n_tiles; ++t) step(t, std::integral_constant<bool, true>());
+    if (SKEW) {
+        wait_vmcnt<0>();
+        __syncthreads();  // every wave's loads of the last V tile landed
+        flush();
+    }
 
     const float lt = halves_sum(st.l);
     const float inv = 1.0f / lt;

@@ -40,10 +40,19 @@ struct RowState {
 // if it jumped by more than kLazyLog2, and the weights made again from S,
 // which is still in registers. Both orders take the same decisions, so
 // the results are the same bits.
-template <int DT, bool CAUSAL, bool EDGE, int NO>
+//
+// `pending` is work that must reach O before any rescale of it (the previous
+// tile's P.V products in a skewed loop): it runs first, and on unmasked
+// tiles in the same block as the weights, so its matrix instructions can
+// issue between the weights' vector instructions.
+struct NoPending {
+    __device__ void operator()() const {}
+};
+template <int DT, bool CAUSAL, bool EDGE, int NO, typename Pending = NoPending>
 __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
                                     v16f32 (&oacc)[NO], RowState& st, float c,
-                                    int k0, int T, int my_q, int hh) {
+                                    int k0, int T, int my_q, int hh,
+                                    Pending pending = Pending()) {
     auto weights = [&](float mc) {
         float t0 = 0.f, t1 = 0.f;
 #pragma unroll
@@ -88,6 +97,7 @@ __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
         }
     };
     if (EDGE) {
+        pending();
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -98,6 +108,7 @@ __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
         rescale();
         st.l += weights(st.mc);
     } else {
+        pending();
         float t = weights(st.mc);
         if (__builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0) {
             rescale();

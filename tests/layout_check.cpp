@@ -855,6 +855,60 @@ static void check_head_dim() {
             CHECK(G::q_col(h, ks) + 8 <= D && G::q_col(h, ks) == 16 * ks + 8 * h, "D%d q_col", D);
 }
 
+// The skewed loop of the other head dims (K in two stages, V in three, each
+// wave waiting only for K(t) at iteration t): simulate one wave's loads in
+// issue order (a wait that leaves w loads in flight completes all older
+// ones) and check that every K(t) read (iteration t) and V(t) read
+// (iteration t + 1, or after the loop; earlier when the wave has no key
+// left to see from tile `skip` on) finds its tile landed in its stage, and
+// that no stage is reloaded while a read of its old tile is still to come.
+static void check_hd_skew_ring(int n, int skip, int ni) {
+    struct Load { int tile; bool v; };
+    std::vector<Load> q;
+    int done = 0;
+    std::vector<int> kst(2, -1), vst(3, -1);
+    std::vector<int> kdone(n, 0), vdone(n, 0);
+    std::vector<int> vread_at(n, -1);  // iteration whose step reads V(t)
+    for (int t = 0; t < n; ++t) {
+        if (t < skip) vread_at[t] = t + 1;  // in iteration t+1 (or the end, n)
+        else vread_at[t] = -1;              // never computed
+    }
+    auto issue = [&](int t, int it) {
+        // K(t) replaces K(t-2): read in iteration t-2 < it
+        const int ko = kst[t % 2];
+        if (ko >= 0) CHECK(ko < it, "hd skew: K stage of %d reloaded at %d", ko, it);
+        const int vo = vst[t % 3];
+        if (vo >= 0 && vread_at[vo] >= 0)
+            CHECK(vread_at[vo] < it, "hd skew: V stage of %d reloaded at %d", vo, it);
+        kst[t % 2] = t; vst[t % 3] = t;
+        for (int i = 0; i < ni; ++i) q.push_back({t, false});
+        for (int i = 0; i < ni; ++i) q.push_back({t, true});
+    };
+    auto wait = [&](int left) {
+        while ((int)q.size() - done > left) {
+            const Load& l = q[done++];
+            if (l.v) vdone[l.tile]++; else kdone[l.tile]++;
+        }
+    };
+    issue(0, -1);
+    for (int t = 0; t < n; ++t) {
+        wait(ni);
+        if (t + 1 < n) issue(t + 1, t);
+        if (t >= skip) {
+            // flush of V(t-1) if it was computed, then nothing
+            if (t == skip && t >= 1) {
+                CHECK(vdone[t - 1] == ni && vst[(t - 1) % 3] == t - 1, "hd skew: flushed V(%d)", t - 1);
+            }
+            continue;
+        }
+        CHECK(kdone[t] == ni && kst[t % 2] == t, "hd skew: K(%d) at %d", t, t);
+        if (t >= 1) CHECK(vdone[t - 1] == ni && vst[(t - 1) % 3] == t - 1, "hd skew: V(%d) at %d", t - 1, t);
+    }
+    wait(0);
+    if (skip >= n && n >= 1)
+        CHECK(vdone[n - 1] == ni && vst[(n - 1) % 3] == n - 1, "hd skew: last V(%d)", n - 1);
+}
+
 // The K / V rings of the 16-bit kernel: simulate one wave's issue order and
 // vmcnt waits (a wait leaving w loads in flight completes all older loads),
 // and check that each read finds its tile landed in its stage and that no
@@ -945,6 +999,9 @@ int main() {
     check_head_dim<64>();
     check_head_dim<128>();
     check_head_dim64_same();
+    for (int n = 1; n <= 40; ++n)
+        for (int skip = 0; skip <= n; ++skip)
+            for (int ni : {1, 2, 4}) check_hd_skew_ring(n, skip, ni);
     check_decode_tile<32>();
     check_decode_tile<64>();
     check_decode_tile<128>();
