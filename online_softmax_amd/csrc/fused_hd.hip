@@ -10,11 +10,15 @@
 // gfx950 design:
 //  - 4 wave64s per workgroup, 32 query rows per wave (128 per workgroup);
 //    Q fragments (D / 16 of them) stay in VGPRs.
-//  - K and V tiles of 64 keys x D arrive by direct buffer loads into a
-//    two-stage LDS ring: one barrier per tile, after which the next tile's
-//    loads are issued and run under this tile's compute. Two workgroups per
-//    CU (LDS: 64 KiB at D = 128), so the other workgroup's waves fill the
-//    matrix cores while a wave does its softmax.
+//  - K and V tiles of 64 keys x D arrive by direct buffer loads into LDS
+//    rings: one barrier per tile, after which the next tile's loads are
+//    issued and run under this tile's compute. Two workgroups per CU, so the
+//    other workgroup's waves fill the matrix cores while a wave does its
+//    softmax.
+//  - D = 32 runs each tile's S, weights and P.V in order (two stages each
+//    for K and V, 16 KiB). D = 128 skews the loop by one tile: the weights of
+//    tile t are made while tile t-1's P.V products run, so one wave's vector
+//    and matrix work overlap too (V in three stages: 80 KiB).
 //  - S^T = K Q^T (D / 16 reduction steps) and O^T += V^T P^T (D / 32 output
 //    tiles, V^T read with ds_read_b64_tr_b16), v_mfma_f32_32x32x16_{bf16,f16}.
 //  - The per-D row swizzles and fragment addresses are HeadDim<D> in
