@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     // Row fragments (A operands) of half mt of a Q or dO tile.
     auto rows4 = [&](const char* tile, int mt, v4u32(&f)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) f[ks] = brow(tile, rb[ks], mt);
+        for (int ks = 0; ks < 4; ++ks) f[ks] = brow_at(lane_tile(tile, rb[ks]), mt);
     };
     // acc = X B for 4 steps (X fragments f, B the lane's K or V row)
     auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
@@ -260,18 +260,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
         if (NEXT) prod4(fs, kf, snext);
         make_pds(u, mt, scur, dp, pf, sf, edge_tag);
         __builtin_amdgcn_sched_barrier(0);
+        const lds_char* dtr[2][2];
+        const lds_char* qtr[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                dtr[ct][hf] = lane_tile(dring[st], tb[ct][hf]);
+                qtr[ct][hf] = lane_tile(qring[st], tb[ct][hf]);
+            }
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dvt[ct] = mfma16<DT>(btr(dring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), pf[kl],
+                dvt[ct] = mfma16<DT>(btr_at(dtr[ct][0], dtr[ct][1], 2 * mt + kl), pf[kl],
                                      dvt[ct]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dkt[ct] = mfma16<DT>(btr(qring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), sf[kl],
+                dkt[ct] = mfma16<DT>(btr_at(qtr[ct][0], qtr[ct][1], 2 * mt + kl), sf[kl],
                                      dkt[ct]);
     };
     // a pipelined tile (S of its first half already in sa; leaves S of the
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
     // Row fragments (A operands) of half nt of a K or V tile.
     auto rows4 = [&](const char* tile, int nt, v4u32(&f)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) f[ks] = brow(tile, rb[ks], nt);
+        for (int ks = 0; ks < 4; ++ks) f[ks] = brow_at(lane_tile(tile, rb[ks]), nt);
     };
     // acc = X B for 4 steps (X fragments f, B the lane's Q or dO row)
     auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
@@ -482,11 +491,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
         if (NEXT) prod4(fs, qf, snext);
         make_ds(u, nt, scur, dp, sf, edge_tag);
         __builtin_amdgcn_sched_barrier(0);
+        const lds_char* ktr[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) ktr[ct][hf] = lane_tile(kring[st], tb[ct][hf]);
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dqt[ct] = mfma16<DT>(btr(kring[st], tb[ct][0], tb[ct][1], 2 * nt + kl), sf[kl],
+                dqt[ct] = mfma16<DT>(btr_at(ktr[ct][0], ktr[ct][1], 2 * nt + kl), sf[kl],
                                      dqt[ct]);
     };
     auto tile = [&](int u, v16f32& sa, v16f32& sb, auto next_tag, auto edge_tag) {

@@ -54,6 +54,33 @@ __device__ inline v4u32 btr(const char* __restrict__ tile, uint32_t b0, uint32_t
     return (v4u32){x2[0], x2[1], y2[0], y2[1]};
 }
 
+// A lane's fragment base in a tile whose ring stage is chosen at run time:
+// the LDS byte address of tile + lane_base, kept opaque to the compiler so
+// that the fragment reads from it take their constant parts (half, step) as
+// instruction offsets. Left alone, the compiler folds those constants into
+// one register per fragment outside the loop and adds the stage to every one
+// of them on every tile.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ inline const lds_char* lane_tile(const char* tile, uint32_t lane_base) {
+    uint32_t t = (uint32_t)(uintptr_t)(lds_void*)tile;  // wave-uniform
+    asm("" : "+s"(t));
+    uint32_t a = t + lane_base;
+    asm("" : "+v"(a));
+    return (const lds_char*)(uintptr_t)a;
+}
+// brow and btr from such bases
+__device__ inline v4u32 brow_at(const lds_char* p, int mt) {
+    typedef __attribute__((address_space(3))) v4u32 lds_v4u32;
+    return *(const lds_v4u32*)(p + kBfragMtStride * mt);
+}
+__device__ inline v4u32 btr_at(const lds_char* p0, const lds_char* p1, int ks) {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + kBtrKsStride * ks));
+    const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1 + kBtrKsStride * ks));
+    const v2u32 x2 = __builtin_bit_cast(v2u32, x), y2 = __builtin_bit_cast(v2u32, y);
+    return (v4u32){x2[0], x2[1], y2[0], y2[1]};
+}
+
 // Store 32 rows x 64 dims held transposed in two accumulators (acc[ct]: lane
 // (row ql, half hh) holds columns 32ct + acc_row(r, hh)), times `mul`.
 template <int DT>
