@@ -138,7 +138,8 @@ size_t attn_naive_workspace_bytes(int B, int H, int T);
  *             accumulated in float32, rounded to nearest even once.
  * workspace : caller-owned device buffer of at least
  *             attn_bwd_workspace_bytes(B, H, T) bytes (16-byte aligned); it
- *             receives delta (float32 [B, H, T]); contents undefined after.
+ *             receives -delta and lse * log2(e) of every row (float32);
+ *             contents undefined after.
  * B, H, T, D, causal, scale, stream: as in attn_fwd_stream.
  * dtype     : ATTN_BF16 or ATTN_F16; ATTN_F32 returns ATTN_ERR_UNSUPPORTED.
  *
@@ -153,8 +154,9 @@ int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,
                     void* workspace, size_t workspace_bytes, int B, int H, int T,
                     int D, int causal, float scale, int dtype, void* stream);
 
-/* Workspace bytes attn_bwd_stream needs: B*H*T*4 rounded up to 256 bytes; 0
- * for sizes < 1 or when the count overflows 64 bits. */
+/* Workspace bytes attn_bwd_stream needs: two float32 values per row (delta
+ * and the scaled lse), 2 * 4 * B*H*T with B*H*T rounded up to a multiple of
+ * 64; 0 for sizes < 1 or when the count overflows 64 bits. */
 size_t attn_bwd_workspace_bytes(int B, int H, int T);
 
 /*

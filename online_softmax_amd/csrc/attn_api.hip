@@ -102,14 +102,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            nullptr);
 }
 
+// Two float32 arrays of one value per row (-delta, lse * log2(e)), each
+// starting on a 256-byte boundary (bwd_ws_stride).
 size_t attn_bwd_workspace_bytes(int B, int H, int T) {
     if (B < 1 || H < 1 || T < 1) return 0;
     uint64_t bh, rows, bytes;
     if (!mul_ok((uint64_t)B, (uint64_t)H, &bh)) return 0;
     if (!mul_ok(bh, (uint64_t)T, &rows)) return 0;
-    if (!mul_ok(rows, 4, &bytes)) return 0;
-    if (bytes > UINT64_MAX - 255) return 0;
-    return (size_t)((bytes + 255) & ~(uint64_t)255);
+    if (rows > ((uint64_t)1 << 60)) return 0;
+    if (!mul_ok((uint64_t)attn::bwd_ws_stride((long long)rows), 8, &bytes)) return 0;
+    return (size_t)bytes;
 }
 
 int attn_bwd_stream(const void* q, const void* k, const void* v, const void* o,

@@ -53,8 +53,9 @@ constexpr float kLog2e = 1.4426950408889634074f;
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_delta16(const uint16_t* __restrict__ o,
                                                    const uint16_t* __restrict__ dout,
-                                                   float* __restrict__ delta,
-                                                   int64_t rows) {
+                                                   const float* __restrict__ lse,
+                                                   float* __restrict__ ndelta,
+                                                   float* __restrict__ lse2, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
     const int part = threadIdx.x & 7;
     float acc = 0.f;
@@ -70,7 +71,10 @@ __global__ __launch_bounds__(256) void bwd_delta16(const uint16_t* __restrict__ 
     acc += __shfl_xor(acc, 1, 8);
     acc += __shfl_xor(acc, 2, 8);
     acc += __shfl_xor(acc, 4, 8);
-    if (row < rows && part == 0) delta[row] = acc;
+    if (row < rows && part == 0) {
+        ndelta[row] = -acc;
+        lse2[row] = lse[row] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -83,7 +87,7 @@ template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ lse2, const float* __restrict__ ndelta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int T, int nkb, float c,
     float scale, uint32_t ksign) {
     constexpr int kStages = 3;
@@ -121,8 +125,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     const uint32_t slice_bytes = (uint32_t)T * (kHeadDim * 2);
     const v4u32_rsrc qrs = buffer_rsrc(q + base, slice_bytes);
     const v4u32_rsrc drs = buffer_rsrc(dout + base, slice_bytes);
-    const v4u32_rsrc lrs = buffer_rsrc(lse + (int64_t)bh * T, (uint32_t)T * 4u);
-    const v4u32_rsrc ers = buffer_rsrc(delta + (int64_t)bh * T, (uint32_t)T * 4u);
+    const v4u32_rsrc lrs = buffer_rsrc(lse2 + (int64_t)bh * T, (uint32_t)T * 4u);
+    const v4u32_rsrc ers = buffer_rsrc(ndelta + (int64_t)bh * T, (uint32_t)T * 4u);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t voff[2];
 #pragma unroll
@@ -131,8 +135,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
     const int nqt = (T + kBwdBlockQ - 1) / kBwdBlockQ;
     const int t0 = bwd_first_qtile(kb, CAUSAL);
     const int n = nqt - t0;
-    // loads of tile u: Q and dO (2 each per wave); lse by wave 0, delta by
-    // wave 1 (one 4-byte-per-lane load each)
+    // loads of tile u: Q and dO (2 each per wave); lse * log2(e) by wave 0,
+    // -delta by wave 1 (one 4-byte-per-lane load each)
     auto issue = [&](int u) {
         const int q0 = (t0 + u) * kBwdBlockQ;
         const int st = u % kStages;
@@ -174,8 +178,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc = mfma16<DT>(f[ks], bf[ks], acc);
     };
-    // P and dS = P (dP - delta) of half mt of query tile u, P = exp2(s c -
-    // lse log2 e) made again, packed into the B operands of dV^T and dK^T
+    // dP - delta of half mt of tile u: the accumulator starts from -delta of
+    // the half's queries (register r: query 32mt + acc_row(r, hh)), so the
+    // products leave dP - delta without a subtraction per score
+    auto dp_minus_delta = [&](int u, int mt, const v4u32(&f)[4], v16f32& acc) {
+        const int st = u % kStages;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const v4f32 e4 = *(const v4f32*)&ering[st][32 * mt + 8 * g + 4 * hh];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * g + i] = e4[i];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16<DT>(f[ks], vf[ks], acc);
+    };
+    // P and dS = P (dP - delta) of half mt of query tile u (dp holds dP -
+    // delta), P = exp2(s c - lse log2 e) made again, packed into the B
+    // operands of dV^T and dK^T
     // (steps 2mt, 2mt + 1). EDGE tiles mask query rows past T and (causal)
     // queries before the lane's key; the lane's queries are
     // q0 + 32mt + acc_row(r, hh).
@@ -193,18 +212,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
         for (int g = 0; g < 4; ++g) {
             const int qi0 = 32 * mt + 8 * g + 4 * hh;  // 4 consecutive queries
             const v4f32 l4 = *(const v4f32*)&lring[st][qi0];
-            const v4f32 e4 = *(const v4f32*)&ering[st][qi0];
             float pv[4], dsv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
-                float p = fast_exp2(fmaf(s[r], c, -l4[i] * kLog2e));
+                float p = fast_exp2(fmaf(s[r], c, -l4[i]));
                 if (EDGE) {  // a masked p is 0, so its dS is too
                     const int off = 32 * mt + 8 * g + i;
                     p = (off < room && (!CAUSAL || off >= lag)) ? p : 0.f;
                 }
                 pv[i] = p;
-                dsv[i] = p * (dp[r] - e4[i]);
+                dsv[i] = p * dp[r];
             }
             // registers r = 4g..4g+3 belong to step 2mt + g/2, dwords
             // 2(g&1), 2(g&1)+1
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
         __builtin_amdgcn_sched_barrier(0);
         v16f32 dp;
         v4u32 pf[2], sf[2];
-        prod4(fd, vf, dp);
+        dp_minus_delta(u, mt, fd, dp);
         if (NEXT) {
             if (mt == 0)
                 rows4(qring[st], 1, fs);
@@ -352,7 +370,7 @@ template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ lse2, const float* __restrict__ ndelta,
     uint16_t* __restrict__ dq, int T, int nq, float c, float scale, uint32_t qsign) {
     constexpr int kStages = 3;
     constexpr int BN = kBlockN16;
@@ -382,10 +400,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
         qf[ks] = x ^ qsign;
         of[ks] = y;
     }
-    float lse2 = 0.f, dl = 0.f;
+    float lq = 0.f, dl = 0.f;  // lse log2(e) and delta of the lane's query
     if (my_q < T) {
-        lse2 = lse[(int64_t)bh * T + my_q] * kLog2e;
-        dl = delta[(int64_t)bh * T + my_q];
+        lq = lse2[(int64_t)bh * T + my_q];
+        dl = -ndelta[(int64_t)bh * T + my_q];
     }
     wait_vmcnt<0>();
 
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
         for (int ks = 0; ks < 4; ++ks) acc = mfma16<DT>(f[ks], bf[ks], acc);
     };
     // dS^T = P (dP - delta) of half nt of key tile u, with P = exp2(s c -
-    // lse2) made again, packed into the B operands of dQ^T (steps 2nt,
+    // lq) made again, packed into the B operands of dQ^T (steps 2nt,
     // 2nt + 1). EDGE tiles mask keys past T and (causal) keys after the
     // lane's query; the lane's keys are k0 + 32nt + acc_row(r, hh).
     auto make_ds = [&](int u, int nt, const v16f32& s, const v16f32& dp, v4u32(&sf)[2],
@@ -449,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 8 * kl + 2 * i + e;
-                    float p = fast_exp2(fmaf(s[r], c, -lse2));
+                    float p = fast_exp2(fmaf(s[r], c, -lq));
                     if (EDGE) {
                         const int key = k0 + acc_row(r, hh);
                         p = (key < T && (!CAUSAL || key <= my_q)) ? p : 0.f;
@@ -548,10 +566,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int BH, int T, int causal, float c, float scale,
+                      float* ws, int BH, int T, int causal, float c, float scale,
                       bool negate, int dt, hipStream_t stream) {
     const uint32_t sign = negate ? 0x80008000u : 0u;
     const int64_t rows = (int64_t)BH * T;
+    float* ndelta = ws;
+    float* lse2 = ws + bwd_ws_stride(rows);
     const int nkb = (T + kBwdBlockKV - 1) / kBwdBlockKV;
     const int nq = (T + kBlockM - 1) / kBlockM;
     const dim3 block(kThreads);
@@ -562,24 +582,24 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     const uint16_t* d16 = (const uint16_t*)dout;
     if (dt == ATTN_DT_BF16) {
         hipLaunchKernelGGL(bwd_delta16<ATTN_DT_BF16>, dim3((unsigned)((rows + 31) / 32)),
-                           dim3(256), 0, stream, o16, d16, delta, rows);
+                           dim3(256), 0, stream, o16, d16, lse, ndelta, lse2, rows);
         auto kv = causal ? bwd_kv16<ATTN_DT_BF16, true> : bwd_kv16<ATTN_DT_BF16, false>;
         hipLaunchKernelGGL(kv, dim3((unsigned)(nkb * BH)), block, 0, stream, q16, k16, v16,
-                           d16, lse, delta, (uint16_t*)dk, (uint16_t*)dv, T, nkb, c, scale,
+                           d16, lse2, ndelta, (uint16_t*)dk, (uint16_t*)dv, T, nkb, c, scale,
                            sign);
         auto qk = causal ? bwd_q16<ATTN_DT_BF16, true> : bwd_q16<ATTN_DT_BF16, false>;
         hipLaunchKernelGGL(qk, dim3((unsigned)(nq * BH)), block, 0, stream, q16, k16, v16,
-                           d16, lse, delta, (uint16_t*)dq, T, nq, c, scale, sign);
+                           d16, lse2, ndelta, (uint16_t*)dq, T, nq, c, scale, sign);
     } else {
         hipLaunchKernelGGL(bwd_delta16<ATTN_DT_F16>, dim3((unsigned)((rows + 31) / 32)),
-                           dim3(256), 0, stream, o16, d16, delta, rows);
+                           dim3(256), 0, stream, o16, d16, lse, ndelta, lse2, rows);
         auto kv = causal ? bwd_kv16<ATTN_DT_F16, true> : bwd_kv16<ATTN_DT_F16, false>;
         hipLaunchKernelGGL(kv, dim3((unsigned)(nkb * BH)), block, 0, stream, q16, k16, v16,
-                           d16, lse, delta, (uint16_t*)dk, (uint16_t*)dv, T, nkb, c, scale,
+                           d16, lse2, ndelta, (uint16_t*)dk, (uint16_t*)dv, T, nkb, c, scale,
                            sign);
         auto qk = causal ? bwd_q16<ATTN_DT_F16, true> : bwd_q16<ATTN_DT_F16, false>;
         hipLaunchKernelGGL(qk, dim3((unsigned)(nq * BH)), block, 0, stream, q16, k16, v16,
-                           d16, lse, delta, (uint16_t*)dq, T, nq, c, scale, sign);
+                           d16, lse2, ndelta, (uint16_t*)dq, T, nq, c, scale, sign);
     }
     return hipGetLastError();
 }

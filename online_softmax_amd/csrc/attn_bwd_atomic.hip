@@ -12,7 +12,7 @@
 // float32 atomics in HBM instead of a second pass.
 //
 // gfx950 design, three launches on one stream:
-//  - bwd_prep16: delta = rowsum(dO * O) and a zero fill of the float32 dQ
+//  - bwd_prep16: -delta = -rowsum(dO * O) and a zero fill of the float32 dQ
 //    copy (a kernel, not a memset, so the sequence can be captured in a graph).
 //  - bwd_kvq16: 4 wave64s, 32 keys per wave, 128 per workgroup, query tiles of
 //    64 through a 2-stage LDS ring loaded one tile ahead by direct buffer
@@ -44,12 +44,12 @@ namespace {
 constexpr float kLog2eA = 1.4426950408889634074f;
 }
 
-// delta (as bwd_delta16) and zeros for the float32 dQ rows: 8 lanes per row,
-// 32 rows per workgroup.
+// -delta (as bwd_delta16) and zeros for the float32 dQ rows: 8 lanes per
+// row, 32 rows per workgroup.
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_prep16(const uint16_t* __restrict__ o,
                                                   const uint16_t* __restrict__ dout,
-                                                  float* __restrict__ delta,
+                                                  float* __restrict__ ndelta,
                                                   float* __restrict__ dq_acc, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
     const int part = threadIdx.x & 7;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void bwd_prep16(const uint16_t* __restrict__ o
     acc += __shfl_xor(acc, 1, 8);
     acc += __shfl_xor(acc, 2, 8);
     acc += __shfl_xor(acc, 4, 8);
-    if (row < rows && part == 0) delta[row] = acc;
+    if (row < rows && part == 0) ndelta[row] = -acc;
 }
 
 // dq = scale * dq_acc rounded to the dtype, 8 values per lane.
@@ -100,7 +100,7 @@ template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ lse, const float* __restrict__ ndelta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dq_acc, int T,
     int nkb, float c, float scale, uint32_t ksign) {
     constexpr int kStages = 2;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
     const v4u32_rsrc qrs = buffer_rsrc(q + base, slice_bytes);
     const v4u32_rsrc drs = buffer_rsrc(dout + base, slice_bytes);
     const v4u32_rsrc lrs = buffer_rsrc(lse + (int64_t)bh * T, (uint32_t)T * 4u);
-    const v4u32_rsrc ers = buffer_rsrc(delta + (int64_t)bh * T, (uint32_t)T * 4u);
+    const v4u32_rsrc ers = buffer_rsrc(ndelta + (int64_t)bh * T, (uint32_t)T * 4u);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t voff[2];
 #pragma unroll
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
 
     auto rows4 = [&](const char* tile, int mt, v4u32(&f)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) f[ks] = brow(tile, rb[ks], mt);
+        for (int ks = 0; ks < 4; ++ks) f[ks] = brow_at(lane_tile(tile, rb[ks]), mt);
     };
     auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
 #pragma unroll
@@ -218,7 +218,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
         for (int g = 0; g < 4; ++g) {
             const int qi0 = 32 * mt + 8 * g + 4 * hh;
             const v4f32 l4 = *(const v4f32*)&lring[st][qi0];
-            const v4f32 e4 = *(const v4f32*)&ering[st][qi0];
             float pv[4], dsv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
                     p = (off < room && (!CAUSAL || off >= lag)) ? p : 0.f;
                 }
                 pv[i] = p;
-                dsv[i] = p * (dp[r] - e4[i]);
+                dsv[i] = p * dp[r];  // dp holds dP - delta
             }
             const int kl = g >> 1, w0 = 2 * (g & 1);
             pf[kl][w0] = pack2<DT>(pv[0], pv[1]);
@@ -251,9 +250,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
         }
         __builtin_amdgcn_sched_barrier(0);
         {
+            // dP - delta: the accumulator starts from -delta of the half's
+            // queries (register r: query 32mt + acc_row(r, hh))
             v4u32 f[4];
             rows4(dring[st], mt, f);
-            prod4(f, vf, dp);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const v4f32 e4 = *(const v4f32*)&ering[st][32 * mt + 8 * g + 4 * hh];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dp[4 * g + i] = e4[i];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) dp = mfma16<DT>(f[ks], vf[ks], dp);
         }
         __builtin_amdgcn_sched_barrier(0);
         v4u32 pf[2], sf[2];
@@ -264,18 +272,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq16(
             *(v2u32*)(sflat + bwd_ds_byte(wave, ql, hh, mt, g)) = w2;
         }
         __builtin_amdgcn_sched_barrier(0);
+        const lds_char* dtr[2][2];
+        const lds_char* qtr[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                dtr[ct][hf] = lane_tile(dring[st], tb[ct][hf]);
+                qtr[ct][hf] = lane_tile(qring[st], tb[ct][hf]);
+            }
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dvt[ct] = mfma16<DT>(btr(dring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), pf[kl],
+                dvt[ct] = mfma16<DT>(btr_at(dtr[ct][0], dtr[ct][1], 2 * mt + kl), pf[kl],
                                      dvt[ct]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                dkt[ct] = mfma16<DT>(btr(qring[st], tb[ct][0], tb[ct][1], 2 * mt + kl), sf[kl],
+                dkt[ct] = mfma16<DT>(btr_at(qtr[ct][0], qtr[ct][1], 2 * mt + kl), sf[kl],
                                      dkt[ct]);
         __builtin_amdgcn_sched_barrier(0);
     };

@@ -259,6 +259,10 @@ struct HeadDim {
 // land on 8 distinct slots) and flips slot bit 2 between rows r and r + 2 of
 // a group of four (the two halves of a transposed read's row quad land on
 // disjoint slots).
+// The backward's row workspace: -delta of every row, then lse * log2(e) of
+// every row, each array starting on a 256-byte boundary (this many floats
+// apart).
+ATTN_HD long long bwd_ws_stride(long long rows) { return (rows + 63) / 64 * 64; }
 constexpr int kBwdBlockKV = 128;  // keys per workgroup of the dK/dV kernel
 constexpr int kBwdBlockQ = 64;    // queries per tile it streams
 ATTN_HD int swz_b(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }

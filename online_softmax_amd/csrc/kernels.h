@@ -24,12 +24,14 @@ hipError_t launch_naive(const float* q, const float* k, const float* v,
                         float* rowsum, int BH, int T, int causal, float scale,
                         hipStream_t stream);
 
-// Backward pass (16-bit dtypes): delta = rowsum(dO * O) into `delta`
-// ([BH, T] float32), then dK/dV and dQ. c = |scale| * log2(e); negate flips
-// the sign of the scores (for scale < 0); scale multiplies dQ and dK.
+// Backward pass (16-bit dtypes): delta = rowsum(dO * O) into the row
+// workspace `ws` (bwd_ws_stride in fused_layout.h: -delta, then lse *
+// log2(e), float32 per row), then dK/dV and dQ. c = |scale| * log2(e);
+// negate flips the sign of the scores (for scale < 0); scale multiplies dQ
+// and dK.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int BH, int T, int causal, float c, float scale,
+                      float* ws, int BH, int T, int causal, float c, float scale,
                       bool negate, int dt, hipStream_t stream);
 
 // Backward pass in one main kernel (16-bit dtypes): delta into `delta` and

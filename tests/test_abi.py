@@ -116,10 +116,12 @@ def test_bwd_rejects_invalid(lib, entry, kw, status):
 
 
 def test_bwd_atomic_workspace_bytes(lib):
-    """delta (padded to 256 bytes) followed by the float32 copy of dQ; a
-    workspace one byte short is refused."""
+    """The split backward's row workspace (attn_bwd_workspace_bytes)
+    followed by the float32 copy of dQ; a workspace one byte short is
+    refused."""
     for B, H, T in [(1, 1, 1), (2, 3, 1000), (4, 12, 8192)]:
-        rows = -(-B * H * T * 4 // 256) * 256
+        rows = osa.attn_bwd_workspace_bytes(B, H, T)
+        assert rows == 2 * -(-B * H * T * 4 // 256) * 256
         need = osa.attn_bwd_atomic_workspace_bytes(B, H, T)
         assert need == rows + B * H * T * 64 * 4
         assert bwd(lib, "attn_bwd_atomic_stream", B=B, H=H, T=T, ws_bytes=need - 1) == -1
@@ -129,7 +131,7 @@ def test_bwd_atomic_workspace_bytes(lib):
 
 def test_bwd_workspace_and_flops():
     for B, H, T in [(1, 1, 1), (2, 3, 1000), (4, 12, 8192)]:
-        assert osa.attn_bwd_workspace_bytes(B, H, T) == -(-B * H * T * 4 // 256) * 256
+        assert osa.attn_bwd_workspace_bytes(B, H, T) == 2 * -(-B * H * T * 4 // 256) * 256
     assert osa.attn_bwd_workspace_bytes(0, 1, 1) == 0
     assert osa.attn_bwd_workspace_bytes(1 << 30, 1 << 30, 1 << 30) == 0
     # five products to the forward's two
