@@ -295,10 +295,24 @@ __global__ __launch_bounds__(256) void decode_combine16(const float* __restrict_
         L += wave_sum(e);
         const int cnt = min(64, nsplit - s0);
         const uint32_t eb = __builtin_bit_cast(uint32_t, e);
-        for (int j = 0; j < cnt; ++j) {
-            const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
+        // eight partials per batch, their loads issued together: split
+        // indices past the last one re-read the last split (in bounds) and
+        // take weight 0 (lanes past nsplit hold e = 0)
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+            float x[8][NPL];
 #pragma unroll
-            for (int i = 0; i < NPL; ++i) acc[i] += ej * op[(int64_t)(s0 + j) * D + 64 * i];
+            for (int j = 0; j < 8; ++j) {
+                const int sj = s0 + min(j0 + j, cnt - 1);
+#pragma unroll
+                for (int i = 0; i < NPL; ++i) x[j][i] = op[(int64_t)sj * D + 64 * i];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float ej =
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, min(j0 + j, 63)));
+#pragma unroll
+                for (int i = 0; i < NPL; ++i) acc[i] += ej * x[j][i];
+            }
         }
     }
     if (D >= 64 || lane < D) {
