@@ -999,6 +999,13 @@ int main() {
     check_head_dim<64>();
     check_head_dim<128>();
     check_head_dim64_same();
+    // the backward's two row arrays: the second starts past the first's last
+    // row, on a 256-byte boundary, with under 256 bytes of padding
+    for (long long rows = 1; rows <= 70000; rows += (rows < 300 ? 1 : 997)) {
+        const long long st = bwd_ws_stride(rows);
+        CHECK(st >= rows && st % 64 == 0 && st - rows < 64, "bwd_ws_stride(%lld)", rows);
+    }
+    CHECK(bwd_ws_stride(4LL * 12 * 8192) == 4LL * 12 * 8192, "bwd_ws_stride of the metric shape");
     for (int n = 1; n <= 40; ++n)
         for (int skip = 0; skip <= n; ++skip)
             for (int ni : {1, 2, 4}) check_hd_skew_ring(n, skip, ni);
