@@ -59,7 +59,9 @@ __device__ inline v4u32 btr(const char* __restrict__ tile, uint32_t b0, uint32_t
 // that the fragment reads from it take their constant parts (half, step) as
 // instruction offsets. Left alone, the compiler folds those constants into
 // one register per fragment outside the loop and adds the stage to every one
-// of them on every tile.
+// of them on every tile. `tile` must be the same for every lane of the wave
+// (a ring stage picked by the loop counter): its offset passes through a
+// scalar register.
 typedef __attribute__((address_space(3))) char lds_char;
 __device__ inline const lds_char* lane_tile(const char* tile, uint32_t lane_base) {
     uint32_t t = (uint32_t)(uintptr_t)(lds_void*)tile;  // wave-uniform
