@@ -173,47 +173,43 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def timed_calls(torch, run, stream, steps, warmup=5, rounds=2):
-    """Time `steps` calls of run() on `stream` with HIP events: a pair around
-    each call (median, min) and a pair around all of them, whose span over
-    the call count is the mean launch duration. Two rounds; the figures are
-    those of the round with the lower mean, and every call of both rounds is
-    kept. (Inside a full benchmark run a single call has been seen to take
-    tens of milliseconds once, on the device side, after the CPU-side
-    correctness checks; the same call alone never does. The second round
-    keeps one such pause from standing for the kernel.)"""
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    best, all_rounds = None, []
-    for _ in range(rounds):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for a, b in ev:
-            a.record(stream)
+def timed_calls(torch, run, stream, steps, warmup=5):
+    """A leg's timing: the time-based warm-up, then `steps` calls timed by
+    time_steps (mean launch duration from the bracketing event pair, the
+    per-call median and min, and how many calls paused on the device)."""
+    calls, _ = warm_up(torch, run, stream, warmup)
+    r = time_steps(torch, run, stream, steps)
+    r["warmup_calls"] = calls
+    return r
+
+
+def warm_up(torch, run, stream, min_calls, min_ms=300.0, batch=10):
+    """Launch run() until at least `min_calls` calls and at least `min_ms` of
+    device time have gone by (HIP events around each batch): clocks and caches
+    settle before anything is timed, whatever the call count asked for.
+    Returns (calls, device ms)."""
+    calls, spent = 0, 0.0
+    while calls < min_calls or spent < min_ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
             run()
-            b.record(stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per = [a.elapsed_time(b) for a, b in ev]
-        r = {"mean": e0.elapsed_time(e1) / steps, "median": statistics.median(per),
-             "min": min(per), "per_call_mean": statistics.fmean(per)}
-        all_rounds.append([round(x, 4) for x in per])
-        if best is None or r["mean"] < best["mean"]:
-            best = r
-    best["per_call_by_round"] = all_rounds
-    return best
-
-
-def time_fused(osa, torch, q, k, v, o, lse, w, steps, warmup):
-    """W warm-up steps, then K timed steps bracketed by synchronisation;
-    each launch is also bracketed by HIP events on the launch stream."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        osa.attn_fwd_stream(q, k, v, o, lse, w.causal, w.scale, stream)
+        b.record(stream)
+        b.synchronize()
+        calls += batch
+        spent += a.elapsed_time(b)
+        if calls >= 100000:
+            break
     torch.cuda.synchronize()
+    return calls, spent
+
+
+def time_steps(torch, run, stream, steps):
+    """K calls timed as one region bracketed by synchronisation (wall clock,
+    the step time), with a HIP event pair on the launch stream around each
+    call and one around all of them (its span over K is the mean launch
+    duration). Calls whose device time exceeds twice the median are counted
+    as device-side pauses; wall time beyond the events' span is host-side."""
     ev = [(torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -222,13 +218,19 @@ def time_fused(osa, torch, q, k, v, o, lse, w, steps, warmup):
     e0.record(stream)
     for a, b in ev:
         a.record(stream)
-        osa.attn_fwd_stream(q, k, v, o, lse, w.causal, w.scale, stream)
+        run()
         b.record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
-    return wall * 1e3 / steps, ms, e0.elapsed_time(e1) / steps
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in ev]
+    span = e0.elapsed_time(e1)
+    med = statistics.median(per)
+    slow = [x for x in per if x > 2.0 * med]
+    return {"wall_ms_per_step": wall / steps, "mean": span / steps, "median": med,
+            "min": min(per), "max": max(per), "per_call": [round(x, 4) for x in per],
+            "device_pauses": len(slow), "device_pause_ms": sum(slow) - med * len(slow),
+            "host_ms": max(0.0, wall - span)}
 
 
 def backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse, steps=20,
@@ -449,7 +451,10 @@ def head_dim_leg(osa, torch, oracle, D, B=4, H=12, T=8192, dtype="bf16", steps=1
     return out
 
 
-PEAK_FP32_VECTOR_TFLOPS = 157.3
+# The float32 FMA rate one VALU instruction per lane reaches (half the
+# published 157.3 TFLOP/s vector peak, which counts packed two-wide FMAs;
+# this library is compiled without packed fp32 instructions).
+PEAK_FP32_FMA_TFLOPS = 78.6
 
 
 def recurrence_leg(osa, torch, oracle, with_oracle=True, steps=20):
@@ -521,12 +526,12 @@ def recurrence_leg(osa, torch, oracle, with_oracle=True, steps=20):
         rec["flop_per_call"] = flops
         achieved = flops / (med * 1e-3) / 1e12
         rec["roofline"] = {"bound": "latency" if label == "page" else "alu",
-                           "achieved": achieved, "peak": PEAK_FP32_VECTOR_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VECTOR_TFLOPS}
+                           "achieved": achieved, "peak": PEAK_FP32_FMA_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_FMA_TFLOPS}
         rec["pass"] = True
         log(f"recurrence {label} {B}x{T}x{H}x{D}: {med * 1e3:.1f} us per call, "
-            f"{achieved:.2f} TFLOP/s ({100 * achieved / PEAK_FP32_VECTOR_TFLOPS:.1f}% of "
-            f"the fp32 vector peak)")
+            f"{achieved:.2f} TFLOP/s ({100 * achieved / PEAK_FP32_FMA_TFLOPS:.1f}% of "
+            f"the one-issue fp32 FMA rate)")
         out[label] = rec
         del args, y
     return out
@@ -590,17 +595,123 @@ def contrast(osa, torch, oracle, steps=10):
     return out
 
 
+def forward_case(osa, torch, oracle, B, H, T, dtype, seed, steps, warmup,
+                 gate_rows=256, label=None):
+    """One fused-forward case other than the headline: seeded inputs, a
+    correctness gate against the double oracle on `gate_rows` sampled rows
+    (0: none), then the time-based warm-up and `steps` timed calls. Returns a
+    small summary (TFLOP/s from the mean launch duration, fraction of the
+    dense peak, the gate's error)."""
+    import numpy as np
+    from online_softmax_amd.inputs import make_qkv, sample_rows
+    dev = torch.device("cuda:0")
+    scale = 0.125
+    q, k, v = make_qkv(B, H, T, 64, dtype, seed)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: osa.attn_fwd_stream(qd, kd, vd, o, lse, True, scale, stream)
+    run()
+    torch.cuda.synchronize()
+    out = {"B": B, "H": H, "T": T}
+    if gate_rows and oracle is not None:
+        rows = sample_rows(B, H, T, gate_rows, seed + 77,
+                           boundaries=(64, 128, T // 2))
+        ro, rl = oracle.attention(q, k, v, True, scale, rows=rows,
+                                  threads=oracle.max_threads())
+        eo = float(np.abs(o.float().cpu().numpy().reshape(-1, 64)[rows] - ro).max())
+        el = float(np.abs(lse.cpu().numpy().reshape(-1)[rows] - rl).max())
+        ok = eo <= BF16_TOL and el <= BF16_TOL and bool(torch.isfinite(o.float()).all())
+        out["gate"] = {"rows": int(len(rows)), "err_o": eo, "err_lse": el, "pass": ok}
+        if not ok:
+            log(f"forward {label or T}: correctness gate FAILED ({eo:.3e}, {el:.3e})")
+            return out
+    r = timed_calls(torch, run, stream, steps, warmup)
+    flops = osa.attn_flops(B, H, T, 64, True)
+    tf = flops / (r["mean"] * 1e-3) / 1e12
+    out.update({"ms": r["mean"], "median_ms": r["median"], "tflops": tf,
+                "frac": tf / PEAK_TFLOPS[dtype], "device_pauses": r["device_pauses"]})
+    log(f"forward {label or ''} B={B} H={H} T={T}: mean {r['mean']:.4f} ms "
+        f"(median {r['median']:.4f}), {tf:.1f} TFLOP/s = {100 * tf / PEAK_TFLOPS[dtype]:.1f}%"
+        + (f", gate err {out['gate']['err_o']:.2e}" if "gate" in out else ""))
+    del qd, kd, vd, o, lse
+    return out
+
+
+def memory_contrast(osa, torch, w):
+    """Device memory held by each forward path at the metric's B, H and T,
+    measured by the caching allocator's peak around one call (the library
+    allocates nothing itself; hipMemGetInfo around the call checks that):
+    the fused path on the bf16 inputs, the naive path in fp32 (its T x T
+    tables live in a caller-owned workspace)."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for path in ("fused", "naive"):
+        dt = torch.bfloat16 if path == "fused" else torch.float32
+        shape = (w.B, w.H, w.T, w.D)
+        q, k, v = (torch.randn(shape, device=dev, dtype=torch.float32).to(dt) for _ in range(3))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        free0 = torch.cuda.mem_get_info(dev)[0]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+        if path == "fused":
+            osa.attn_fwd_stream(q, k, v, o, lse, True, w.scale)
+        else:
+            ws = torch.empty(osa.attn_naive_workspace_bytes(w.B, w.H, w.T),
+                             dtype=torch.uint8, device=dev)
+            osa.attn_naive_fwd(q, k, v, o, lse, ws, True, w.scale)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev)
+        free1 = torch.cuda.mem_get_info(dev)[0]
+        out[path] = {"dtype": "bf16" if path == "fused" else "f32",
+                     "inputs_B": base, "held_beyond_inputs_B": peak - base,
+                     "output_B": o.numel() * o.element_size() + lse.numel() * 4,
+                     "driver_free_drop_B": max(0, free0 - free1)}
+        log(f"memory, {path} path at B={w.B} H={w.H} T={w.T}: inputs {base / 2**20:.1f} MiB, "
+            f"held beyond them {(peak - base) / 2**20:.1f} MiB")
+        del q, k, v, o, lse
+        if path == "naive":
+            del ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def compact(d, nd=4):
+    """Round floats for the one-line summary."""
+    if isinstance(d, float):
+        return float(f"{d:.{nd}g}")
+    if isinstance(d, dict):
+        return {k: compact(v, nd) for k, v in d.items()}
+    if isinstance(d, (list, tuple)):
+        return [compact(v, nd) for v in d]
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="warm-up calls (at least; warm-up also lasts at least "
+                         "300 ms of device time)")
     ap.add_argument("--workload", default=None,
                     help="a name from online_softmax_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-rows", type=int, default=196608,
                     help="oracle sample size for the CPU baseline")
+    ap.add_argument("--detail", default=None,
+                    help="also write every figure of the run to this JSON file")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contrast", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sequence-length sweep and the long context")
+    ap.add_argument("--long-131k", action="store_true",
+                    help="also time the 131072-token long-context case")
+    ap.add_argument("--no-memory", action="store_true",
+                    help="skip the fused/naive device-memory contrast")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass leg")
     ap.add_argument("--no-decode", action="store_true",
@@ -643,9 +754,11 @@ def main():
     osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale)
     torch.cuda.synchronize()
 
-    cpu, parity = None, None
+    oracle = None
     if not a.no_cpu_baseline:
         import oracle
+    cpu, parity = None, None
+    if oracle is not None:
         log(f"oracle on {a.cpu_rows} sampled rows (correctness gate and CPU "
             "baseline) ...")
         cpu, parity = cpu_baseline(oracle, q, k, v, o, lse, w, a.cpu_rows, 9001)
@@ -660,16 +773,40 @@ def main():
             log("correctness gate FAILED: not timing a wrong kernel")
             sys.exit(3)
 
-    ms_step, launch_ms, avg_launch = time_fused(osa, torch, qd, kd, vd, o, lse, w,
-                                                a.steps, a.warmup)
+    # The headline: W warm-up calls (and at least 300 ms of them), then K
+    # timed steps bracketed by synchronisation.
+    stream = torch.cuda.current_stream()
+    run = lambda: osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale, stream)
+    warm_calls, warm_ms = warm_up(torch, run, stream, a.warmup)
+    t = time_steps(torch, run, stream, a.steps)
     flops = osa.attn_flops(w.B, w.H, w.T, w.D, w.causal)
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch * 1e-3) / 1e12
+    value = flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (t["mean"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"fused: {ms_step:.4f} ms/step wall, launch median "
-        f"{statistics.median(launch_ms):.4f} ms (min {min(launch_ms):.4f}, mean "
-        f"{avg_launch:.4f}), {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% "
-        f"of {peak} TFLOP/s")
+    log(f"fused: warm-up {warm_calls} calls ({warm_ms:.0f} ms); {t['wall_ms_per_step']:.4f} "
+        f"ms/step wall, launch mean {t['mean']:.4f} ms (median {t['median']:.4f}, min "
+        f"{t['min']:.4f}, max {t['max']:.4f}); {t['device_pauses']} device pauses, "
+        f"{t['host_ms']:.3f} ms host-side; {achieved:.1f} TFLOP/s = "
+        f"{100 * achieved / peak:.1f}% of {peak} TFLOP/s")
+    del o, lse
+
+    sweep = long_ctx = None
+    if not a.no_sweep and w.name == METRIC_WORKLOAD:
+        sweep = {}
+        for T in (1024, 2048, 4096, 8192, 16384):
+            sweep[str(T)] = forward_case(osa, torch, oracle, 4, 12, T, "bf16", 2500 + T,
+                                         steps=20, warmup=20, label="sweep")
+        long_ctx = {}
+        for name in ("long_b1h16_t32768_bf16",) + (("long_b1h16_t131072_bf16",)
+                                                   if a.long_131k else ()):
+            lw = WORKLOADS[name]
+            long_ctx[str(lw.T)] = forward_case(
+                osa, torch, oracle, lw.B, lw.H, lw.T, lw.dtype, lw.seed,
+                steps=10 if lw.T <= 32768 else 3, warmup=3, gate_rows=4096, label=name)
+
+    mem = None
+    if not a.no_memory:
+        mem = memory_contrast(osa, torch, w)
 
     if a.copy_mib > 0:  # reference kernel of known size for byte counters
         src = torch.empty(a.copy_mib * 2**20, dtype=torch.uint8, device=dev)
@@ -678,81 +815,106 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {a.copy_mib} MiB x 3 (PMC reference)")
+        del src, dst
 
     bwd = bwd_atomic = None
     if not a.no_backward and w.dtype != "f32":
-        import oracle
         cache = {}
-        bwd = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
-                           with_oracle=not a.no_cpu_baseline, cache=cache)
-        bwd_atomic = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, o, lse,
-                                  with_oracle=not a.no_cpu_baseline, atomic=True,
-                                  cache=cache)
+        bwd = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd, *fresh_out(osa, torch, qd, kd, vd, w),
+                           with_oracle=oracle is not None, cache=cache)
+        bwd_atomic = backward_leg(osa, torch, oracle, w, q, k, v, qd, kd, vd,
+                                  *fresh_out(osa, torch, qd, kd, vd, w),
+                                  with_oracle=oracle is not None, atomic=True, cache=cache)
         bwd_atomic.pop("cpu_baseline", None)
 
     dec = dec128 = None
     if not a.no_decode:
-        import oracle
-        dec = decode_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
-        dec128 = decode_leg(osa, torch, oracle, D=128, with_oracle=not a.no_cpu_baseline)
+        dec = decode_leg(osa, torch, oracle, with_oracle=oracle is not None)
+        dec128 = decode_leg(osa, torch, oracle, D=128, with_oracle=oracle is not None)
         dec128.pop("cpu_baseline", None)
 
     hds = None
     if not a.no_head_dims:
-        import oracle
-        hds = {str(D): head_dim_leg(osa, torch, oracle, D, with_oracle=not a.no_cpu_baseline)
+        hds = {str(D): head_dim_leg(osa, torch, oracle, D, with_oracle=oracle is not None)
                for D in (32, 128)}
 
     recur = None
     if not a.no_recurrence:
-        import oracle
-        recur = recurrence_leg(osa, torch, oracle, with_oracle=not a.no_cpu_baseline)
+        recur = recurrence_leg(osa, torch, oracle, with_oracle=oracle is not None)
 
     extra = None
-    if not a.no_contrast:
-        import oracle
+    if not a.no_contrast and oracle is not None:
         extra = contrast(osa, torch, oracle)
 
     single = None
-    if not a.no_cpu_baseline:
-        import oracle
+    if oracle is not None:
         single = oracle_single_core(oracle)
 
     kname = osa.attn_kernel_name({"bf16": 0, "f16": 2, "f32": 4}[w.dtype] +
                                  (0 if w.causal else 1))
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": measured_traffic(), "kernel": kname,
+                "launch_ms": {"mean": t["mean"], "median": t["median"]}}
+    detail = {
+        "metric": METRIC, "value": value, "warmup_calls": warm_calls, "warmup_ms": warm_ms,
+        "timing": t, "roofline": dict(roofline, algorithmic_flop_per_launch=flops,
+                                      traffic_arith_B=traffic_f),
+        "cpu_baseline": cpu, "parity": parity, "kernels": kernels, "sweep": sweep,
+        "long_context": long_ctx, "memory": mem, "backward": bwd,
+        "backward_atomic": bwd_atomic, "cpu_single_core": single, "decode": dec,
+        "decode_d128": dec128, "head_dims": hds, "gated_recurrence": recur,
+        "contrast_fp32_single_head": extra, "kernel_source_sha256": kernel_source_hash()}
+    log("bench detail: " + json.dumps(detail))
+    if a.detail:
+        with open(a.detail, "w") as f:
+            json.dump(detail, f, indent=1)
+
+    def leg(x, key="roofline"):
+        if not x or not x.get("pass", True) or key not in x:
+            return None if not x else {"pass": x.get("pass")}
+        r = x[key]
+        return [r["achieved"], r["unit"], r["frac"]]
+
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step,
+        "steps": a.steps, "warmup": a.warmup, "warmup_calls": warm_calls,
+        "ms_per_step": t["wall_ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic: seeded torch.randn N(0,1) fp32, rounded (RNE) to "
-                f"{w.dtype}",
+        "dtype": w.dtype, "data": f"synthetic: seeded N(0,1) fp32 rounded to {w.dtype}",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
-                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(),
-                     "kernel": kname,
-                     "launch_ms": {"mean": avg_launch,
-                                   "median": statistics.median(launch_ms),
-                                   "min": min(launch_ms)},
-                     "algorithmic_flop_per_launch": flops,
-                     "traffic_arith_B": traffic_f},
-        "cpu_baseline": cpu,
-        "parity": parity,
-        "kernels": kernels,
-        "backward": bwd,
-        "backward_atomic": bwd_atomic,
-        "cpu_single_core": single,
-        "decode": dec,
-        "decode_d128": dec128,
-        "head_dims": hds,
-        "gated_recurrence": recur,
-        "contrast_fp32_single_head": extra,
-        "kernel_source_sha256": kernel_source_hash(),
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": None if cpu is None else {
+            "value": cpu["value"], "unit": cpu["unit"], "cores": cpu["cores"],
+            "kind": "oracle", "sample": f"{parity['rows']} seeded rows of {w.name}"},
+        "parity": None if parity is None else
+            f"{parity['rows']} rows vs oracle: max|dO| {parity['max_abs_err_o']:.2e}, "
+            f"max|dlse| {parity['max_abs_err_lse']:.2e}, bound {parity['bound']:g}, "
+            + ("pass" if parity["pass"] else "FAIL"),
+        "pauses": {"device": t["device_pauses"], "host_ms": t["host_ms"]},
+        "sweep_tflops": None if sweep is None else
+            {T: s.get("tflops") for T, s in sweep.items()},
+        "long_context": None if long_ctx is None else
+            {T: {"tflops": s.get("tflops"), "frac": s.get("frac"),
+                 "gate_err": s.get("gate", {}).get("err_o")} for T, s in long_ctx.items()},
+        "memory_beyond_inputs_B": None if mem is None else
+            {p: m["held_beyond_inputs_B"] for p, m in mem.items()},
+        "legs": {"bwd": leg(bwd), "bwd_atomic": leg(bwd_atomic), "decode": leg(dec),
+                 "decode_d128": leg(dec128),
+                 "d32": leg((hds or {}).get("32")), "d128": leg((hds or {}).get("128")),
+                 "recurrence": leg((recur or {}).get("throughput"))},
     }
-    print(json.dumps(line), flush=True)
+    sys.stderr.flush()
+    print(json.dumps(compact(line), separators=(",", ":")), flush=True)
+
+
+def fresh_out(osa, torch, qd, kd, vd, w):
+    """O and lse of the metric workload for the backward legs."""
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=qd.device)
+    osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+    return o, lse
 
 
 if __name__ == "__main__":

@@ -201,8 +201,14 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
                 const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
                 oacc[mt] = mfma16<DT>((v4u32){a2[0], a2[1], b2[0], b2[1]}, pf[ks], oacc[mt]);
             }
-        // the stage of tile t is read (its fragments are in registers): refill
-        if (t + 2 < n) issue(t + 2);
+        // refill the stage of tile t once its fragment reads have returned:
+        // the direct loads write the LDS behind the reads' backs, so the
+        // reads (issued above, consumed by matrix instructions the compiler
+        // may place after this point) are waited for first
+        if (t + 2 < n) {
+            wait_lgkmcnt0();
+            issue(t + 2);
+        }
     }
 
     // merge the four waves' states through LDS (the ring is free now)

@@ -150,6 +150,12 @@ __device__ inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until every LDS (and scalar memory) operation of this wave has
+// completed (vector-memory and export counters untouched).
+__device__ inline void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Wait until at most `in_flight` (0, 2, 4 or 6: whole load batches) of this
 // wave's loads are pending.
 __device__ inline void wait_loads(int in_flight) {

@@ -394,7 +394,6 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
     return bad ? -2 : 0;
 }
 
-/* Number of OpenMP threads a parallel region would use by default. */
 /* The gated linear recurrence above, for every (batch, head); inputs
  * float32 [B, T, H, D], output y double [B, T, H, D]. Returns 0, or -1 for
  * invalid sizes or an allocation failure. */
@@ -403,13 +402,17 @@ int oracle_gated_recurrence(const float* q, const float* k, const float* v,
                             int64_t D, double* y, int nthreads) {
     if (B < 1 || T < 1 || H < 1 || D < 1) return -1;
     int failed = 0;
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
     for (int64_t bh = 0; bh < B * H; ++bh) {
         const int64_t b = bh / H, h = bh % H;
         double* S = (double*)calloc((size_t)(D * D), sizeof(double));
         if (!S) {
+#ifdef _OPENMP
 #pragma omp atomic write
+#endif
             failed = 1;
             continue;
         }
@@ -427,9 +430,11 @@ int oracle_gated_recurrence(const float* q, const float* k, const float* v,
         }
         free(S);
     }
+    (void)nthreads;
     return failed ? -1 : 0;
 }
 
+/* Number of OpenMP threads a parallel region would use by default. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

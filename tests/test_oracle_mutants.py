@@ -89,8 +89,9 @@ RECURRENCE_MUTANTS = [
     ("rec_state_not_reset", [("double* S = (double*)calloc((size_t)(D * D), sizeof(double));",
                               "static double Sbuf[4096]; double* S = D * D <= 4096 ? Sbuf : "
                               "(double*)calloc((size_t)(D * D), sizeof(double));"),
-                             ("        free(S);\n    }\n    return failed",
-                              "        if (S != Sbuf) free(S);\n    }\n    return failed")]),
+                             ("        free(S);\n    }\n    (void)nthreads;\n    return failed",
+                              "        if (S != Sbuf) free(S);\n    }\n    (void)nthreads;\n"
+                              "    return failed")]),
 ]
 
 CASES = [(n, e, "test_oracle_pins.py") for n, e in MUTANTS] + \
