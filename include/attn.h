@@ -226,6 +226,31 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
 size_t attn_decode_workspace_bytes(int B, int H, int Tq, int Tk, int D);
 
 /*
+ * attn_decode_noalloc_stream - attn_decode_stream without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). It allocates
+ * nothing and calls no allocating routine: the split partials and one
+ * counter per (batch, head, 32-query tile) live in the library's own static
+ * device scratch of ATTN_DECODE_SCRATCH_BYTES (4.03 MiB; each GPU the library
+ * runs on holds one copy until the process ends), and the last workgroup of
+ * each tile to finish merges the partials itself, so the call is one kernel
+ * launch (two on a device's first call, which also clears the counters).
+ *
+ * Arguments, layouts and results are those of attn_decode_stream minus the
+ * workspace. Every call on one GPU uses that GPU's one scratch: calls that
+ * overlap on one GPU (concurrent streams or host threads) race and must be
+ * serialised by the caller. The counters are back at zero when a call ends.
+ * Returns ATTN_OK once enqueued, or an error status with nothing enqueued:
+ * the errors of attn_decode_stream, and ATTN_ERR_UNSUPPORTED when the sizes
+ * need more scratch than ATTN_DECODE_SCRATCH_BYTES (more than 256 tiles
+ * with the keys split, which the split plan never chooses).
+ */
+#define ATTN_DECODE_SCRATCH_BYTES 4228096u
+int attn_decode_noalloc_stream(const void* q, const void* k, const void* v, void* o,
+                               float* lse, int B, int H, int Tq, int Tk, int D, int causal,
+                               float scale, int dtype, void* stream);
+
+/*
  * attn_gated_recurrence_stream - the gated linear recurrence of the
  * POPCORNBENCH transcript "Kimi-K2.6 l2 p24" (no softmax): per (batch,
  * head) a D x D state S starts at zero and, for t = 0 .. T-1 in order,

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     ATTN_F32, ATTN_OK, ATTN_PATH_FUSED, ATTN_PATH_NAIVE, EXPORTS, LIBRARY,
     AttnError, attention, attention_backward, attention_decode, attn_bwd_flops,
     attn_bwd_stream, attn_bwd_atomic_stream, attn_bwd_atomic_workspace_bytes,
-    attn_decode_stream, attn_decode_workspace_bytes,
+    attn_decode_stream, attn_decode_workspace_bytes, attn_decode_noalloc_stream,
     attn_bwd_workspace_bytes, attn_flops, attn_fused_tile, attn_fwd,
     attn_fwd_stream, attn_kernel_attributes, attn_kernel_count,
     attn_kernel_name, attn_last_hip_error, attn_naive_fwd,

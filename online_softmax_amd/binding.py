@@ -30,7 +30,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
            "attn_flops", "attn_status_string", "attn_last_hip_error",
            "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
            "attn_fused_tile", "attn_gated_recurrence_stream",
-           "attn_gated_recurrence_flops")
+           "attn_gated_recurrence_flops", "attn_decode_noalloc_stream")
 
 
 class AttnError(RuntimeError):
@@ -88,6 +88,7 @@ def load(path: str = LIBRARY):
         lib.attn_decode_stream.argtypes = [P] * 6 + [S, I, I, I, I, I, I, F, I, P]
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
         lib.attn_decode_workspace_bytes.restype = S
+        lib.attn_decode_noalloc_stream.argtypes = [P] * 5 + [I, I, I, I, I, I, F, I, P]
         lib.attn_gated_recurrence_stream.argtypes = [P] * 5 + [I, I, I, I, P]
         lib.attn_gated_recurrence_flops.argtypes = [I, I, I, I]
         lib.attn_gated_recurrence_flops.restype = ctypes.c_double
@@ -287,6 +288,24 @@ def attn_decode_stream(q, k, v, o, lse, workspace, causal: bool, scale: float,
                                    int(bool(causal)), float(scale), dtype_code(q),
                                    _stream(stream, q.device))
     _check(st, "attn_decode_stream")
+
+
+def attn_decode_noalloc_stream(q, k, v, o, lse, causal: bool, scale: float, stream=None):
+    """Decode as attn_decode_stream, with the library's own scratch instead
+    of a workspace (no allocation; calls on one GPU must not overlap)."""
+    B, H, Tq, D = _dims(q)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Tk, D]")
+    Tk = int(k.shape[2])
+    _expect(q, "q", q.shape, q.dtype, q.device)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    for name, t in (("k", k), ("v", v)):
+        _expect(t, name, (B, H, Tk, D), q.dtype, q.device)
+    _expect_lse(lse, (B, H, Tq), q.device)
+    st = _lib().attn_decode_noalloc_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                           B, H, Tq, Tk, D, int(bool(causal)), float(scale),
+                                           dtype_code(q), _stream(stream, q.device))
+    _check(st, "attn_decode_noalloc_stream")
 
 
 def attn_gated_recurrence_stream(q, k, v, gate, y, stream=None):

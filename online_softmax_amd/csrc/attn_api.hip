@@ -250,6 +250,43 @@ int attn_decode_stream(const void* q, const void* k, const void* v, void* o, flo
     return ATTN_OK;
 }
 
+static_assert(attn::kDecodeScratchBytes == ATTN_DECODE_SCRATCH_BYTES,
+              "the header states the scratch size");
+
+int attn_decode_noalloc_stream(const void* q, const void* k, const void* v, void* o,
+                               float* lse, int B, int H, int Tq, int Tk, int D, int causal,
+                               float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
+    if (B < 1 || H < 1 || Tq < 1 || Tk < 1 || D < 1) return ATTN_ERR_INVALID;
+    if (Tq > Tk) return ATTN_ERR_INVALID;
+    int st = check_shape(B, H, Tk, D, fwd16_head_dim(D));
+    if (st != ATTN_OK) return st;
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return ATTN_ERR_INVALID;
+    if (lse && !aligned4(lse)) return ATTN_ERR_INVALID;
+    if ((uint64_t)Tk * D * 2 > UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    uint64_t bh;
+    if (!mul_ok((uint64_t)B, (uint64_t)H, &bh) || bh > (uint64_t)INT32_MAX)
+        return ATTN_ERR_UNSUPPORTED;
+    const int BH = (int)bh;
+    int nsplit, chunk;
+    attn::decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    const uint64_t nqt = ((uint64_t)Tq + 31) / 32;
+    if ((uint64_t)BH * nqt * nsplit > kMaxFusedWorkgroups) return ATTN_ERR_UNSUPPORTED;
+    const size_t need = attn::decode_scratch_need(BH, Tq, Tk, D);
+    if (need == 0 || need > attn::kDecodeScratchBytes) return ATTN_ERR_UNSUPPORTED;
+    const double c = fabs((double)scale) * 1.4426950408889634073599;
+    if (!isfinite((float)c)) return ATTN_ERR_INVALID;
+    const hipError_t e = attn::launch_decode_noalloc(q, k, v, o, lse, BH, Tq, Tk, D,
+                                                     causal ? 1 : 0, (float)c, scale < 0.0f,
+                                                     dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATTN_OK;
+}
+
 int attn_gated_recurrence_stream(const float* q, const float* k, const float* v,
                                  const float* gate, float* y, int B, int T, int H, int D,
                                  void* stream) {
@@ -403,7 +440,7 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
            attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels +
-           attn::kBwdAtomicKernels + attn::kDecodeHdKernels;
+           attn::kBwdAtomicKernels + attn::kDecodeHdKernels + attn::kDecodeMergedKernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -443,7 +480,13 @@ const char* attn_kernel_name(int kernel) {
         "decode_split16<f16, full, 32>", "decode_combine16<f16, 32>",
         "decode_split16<bf16, causal, 128>", "decode_split16<bf16, full, 128>",
         "decode_combine16<bf16, 128>", "decode_split16<f16, causal, 128>",
-        "decode_split16<f16, full, 128>", "decode_combine16<f16, 128>"};
+        "decode_split16<f16, full, 128>", "decode_combine16<f16, 128>",
+        "decode_merged16<bf16, causal>", "decode_merged16<bf16, full>",
+        "decode_merged16<f16, causal>", "decode_merged16<f16, full>",
+        "decode_merged16<bf16, causal, 32>", "decode_merged16<bf16, full, 32>",
+        "decode_merged16<f16, causal, 32>", "decode_merged16<f16, full, 32>",
+        "decode_merged16<bf16, causal, 128>", "decode_merged16<bf16, full, 128>",
+        "decode_merged16<f16, causal, 128>", "decode_merged16<f16, full, 128>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -456,6 +499,7 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     const int rec0 = hd0 + attn::kHdKernels;
     const int bat0 = rec0 + attn::kRecurrenceKernels;
     const int dhd0 = bat0 + attn::kBwdAtomicKernels;
+    const int dmg0 = dhd0 + attn::kDecodeHdKernels;
     const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
@@ -463,7 +507,8 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
                      : kernel < rec0 ? attn::hd_kernel_ptr(kernel - hd0)
                      : kernel < bat0 ? attn::recurrence_kernel_ptr(kernel - rec0)
                      : kernel < dhd0 ? attn::bwd_atomic_kernel_ptr(kernel - bat0)
-                                     : attn::decode_kernel_ptr(6 + kernel - dhd0);
+                     : kernel < dmg0 ? attn::decode_kernel_ptr(6 + kernel - dhd0)
+                                     : attn::decode_merged_kernel_ptr(kernel - dmg0);
     hipFuncAttributes fa;
     hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return hip_fail(e);

@@ -25,6 +25,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fused_layout.h"
 #include "gfx950.h"
 #include "kernels.h"
@@ -58,11 +60,20 @@ __device__ inline void dec_load(v4u32_rsrc rs, const uint32_t (&voff)[dec_instr<
 // where the split holds no visible key of the row). rows = BH * Tq.
 // At D = 128 the ring (128 KiB) leaves room for one workgroup per CU, which
 // is all the split plan launches.
-template <int DT, bool CAUSAL, int D>
+//
+// MERGED (the no-allocation entry point): the partials live in the library's
+// own scratch, and the last workgroup of a query tile to finish merges them
+// into o and lse itself (one launch, no combine kernel). Each tile has a
+// counter that starts at 0; a workgroup publishes its partial (release at
+// device scope), then adds 1 to the counter; the one that reads nsplit - 1
+// acquires, merges, and sets the counter back to 0 for the next call. With
+// one split the workgroup writes o and lse directly.
+template <int DT, bool CAUSAL, int D, bool MERGED = false>
 __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
-    int Tq, int Tk, int nqt, int nsplit, int chunk, float c, uint32_t qsign) {
+    int Tq, int Tk, int nqt, int nsplit, int chunk, float c, uint32_t qsign,
+    uint16_t* __restrict__ o, float* __restrict__ lse, uint32_t* __restrict__ counters) {
     using G = HeadDim<D>;
     constexpr int kStages = 2;
     constexpr int NI = dec_instr<D>();     // direct loads per K or V tile
@@ -250,11 +261,58 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
                 for (int j = 0; j < kDims; ++j) acc[j] += e * so[(w * kDecTile + rq) * D + d0 + j];
             }
         }
-        const int64_t p = ((int64_t)bh * Tq + qrow) * nsplit + split;
         const float inv = L > 0.f ? 1.0f / L : 0.f;
+        if (MERGED && nsplit == 1) {  // the whole row: the output itself
+            const int64_t row = (int64_t)bh * Tq + qrow;
 #pragma unroll
-        for (int j = 0; j < kDims; ++j) o_part[p * D + d0 + j] = acc[j] * inv;
-        if ((tid & 7) == 0) lse_part[p] = L > 0.f ? (M + log2f(L)) * kDecLn2 : -INFINITY;
+            for (int j = 0; j < kDims; j += 2)
+                *(uint32_t*)(o + row * D + d0 + j) = pack2<DT>(acc[j] * inv, acc[j + 1] * inv);
+            if ((tid & 7) == 0 && lse != nullptr) lse[row] = (M + log2f(L)) * kDecLn2;
+        } else {
+            const int64_t p = ((int64_t)bh * Tq + qrow) * nsplit + split;
+#pragma unroll
+            for (int j = 0; j < kDims; ++j) o_part[p * D + d0 + j] = acc[j] * inv;
+            if ((tid & 7) == 0) lse_part[p] = L > 0.f ? (M + log2f(L)) * kDecLn2 : -INFINITY;
+        }
+    }
+    if constexpr (MERGED) {
+        if (nsplit == 1) return;
+        __shared__ int is_last;
+        __threadfence();  // this workgroup's partials, visible device-wide
+        __syncthreads();
+        const int tile = blockIdx.x / nsplit;  // (slice, query tile)
+        if (tid == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_ACQ_REL,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            is_last = before == (uint32_t)(nsplit - 1);
+        }
+        __syncthreads();
+        if (!is_last) return;
+        __threadfence();  // every split's partials before they are read
+        if (qrow < Tq) {
+            const int64_t row = (int64_t)bh * Tq + qrow;
+            const float* lp = lse_part + row * nsplit;
+            const float* op = o_part + row * nsplit * D + d0;
+            float M = -INFINITY;
+            for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, lp[sp]);
+            float L = 0.f, acc[kDims];
+#pragma unroll
+            for (int j = 0; j < kDims; ++j) acc[j] = 0.f;
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const float ls = lp[sp];
+                const float e = ls == -INFINITY ? 0.f : __expf(ls - M);
+                L += e;
+#pragma unroll
+                for (int j = 0; j < kDims; ++j) acc[j] += e * op[(int64_t)sp * D + j];
+            }
+            const float inv = 1.0f / L;
+#pragma unroll
+            for (int j = 0; j < kDims; j += 2)
+                *(uint32_t*)(o + row * D + d0 + j) = pack2<DT>(acc[j] * inv, acc[j + 1] * inv);
+            if ((tid & 7) == 0 && lse != nullptr) lse[row] = M + logf(L);
+        }
+        if (tid == 0)  // the tile's counter back to 0 for the next call
+            __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -336,7 +394,8 @@ void launch_decode_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
                      dim3 cgrid, int64_t rows, hipStream_t stream) {
     auto fn = causal ? decode_split16<DT, true, D> : decode_split16<DT, false, D>;
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q, k, v, o_part, lse_part, Tq, Tk,
-                       nqt, nsplit, chunk, c, sign);
+                       nqt, nsplit, chunk, c, sign, (uint16_t*)nullptr, (float*)nullptr,
+                       (uint32_t*)nullptr);
     hipLaunchKernelGGL((decode_combine16<DT, D>), cgrid, dim3(256), 0, stream, o_part,
                        lse_part, o, lse, rows, nsplit);
 }
@@ -371,6 +430,105 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Decode without allocation: the library's own scratch holds the per-tile
+// counters (kDecodeCounters uint32, zero between calls) and, after them, the
+// split partials (o_part, then lse_part). Every GPU the library runs on holds
+// one copy until the process ends; calls on one GPU share it, so calls that
+// overlap on one GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+__global__ __launch_bounds__(256) void decode_scratch_clear(uint32_t* __restrict__ counters) {
+    for (int i = threadIdx.x; i < kDecodeCounters; i += 256) counters[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+unsigned char* g_scratch[kMaxDevices] = {};  // device address of scratch, per device
+}  // namespace
+
+// The device address of the current device's scratch: looked up once per
+// device (hipGetSymbolAddress with that device current), when its counters
+// are also cleared on `stream`; host code uses this address, never the
+// array's name.
+static hipError_t decode_scratch_address(unsigned char** out, hipStream_t stream) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_scratch_clear, dim3(1), dim3(256), 0, stream, (uint32_t*)p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = (unsigned char*)p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+template <int DT, int D>
+static void launch_decode_merged_d(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* o, float* lse, float* o_part, float* lse_part,
+                                   uint32_t* counters, int Tq, int Tk, int nqt, int nsplit,
+                                   int chunk, int causal, float c, uint32_t sign, dim3 grid,
+                                   hipStream_t stream) {
+    auto fn = causal ? decode_split16<DT, true, D, true> : decode_split16<DT, false, D, true>;
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, stream, q, k, v, o_part, lse_part, Tq, Tk,
+                       nqt, nsplit, chunk, c, sign, o, lse, counters);
+}
+
+size_t decode_scratch_need(int BH, int Tq, int Tk, int D) {
+    int nsplit, chunk;
+    decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    if (nsplit == 1) return kDecodeCounterBytes;
+    const uint64_t nqt = ((uint64_t)Tq + kDecTile - 1) / kDecTile;
+    if ((uint64_t)BH * nqt > (uint64_t)kDecodeCounters) return 0;
+    const uint64_t parts = (uint64_t)BH * Tq * nsplit;
+    return kDecodeCounterBytes + parts * (uint64_t)(D + 1) * 4;
+}
+
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int BH, int Tq, int Tk, int D, int causal,
+                                 float c, bool negate_q, int dt, hipStream_t stream) {
+    unsigned char* base = nullptr;
+    hipError_t e = decode_scratch_address(&base, stream);
+    if (e != hipSuccess) return e;
+    int nsplit, chunk;
+    decode_plan(BH, Tq, Tk, &nsplit, &chunk);
+    const int nqt = (Tq + kDecTile - 1) / kDecTile;
+    const uint32_t sign = negate_q ? 0x80008000u : 0u;
+    const dim3 grid((unsigned)(BH * nqt * nsplit));
+    const uint64_t parts = (uint64_t)BH * Tq * nsplit;
+    uint32_t* counters = (uint32_t*)base;
+    float* o_part = (float*)(base + kDecodeCounterBytes);
+    float* lse_part = o_part + parts * D;
+    const uint16_t* q16 = (const uint16_t*)q;
+    const uint16_t* k16 = (const uint16_t*)k;
+    const uint16_t* v16 = (const uint16_t*)v;
+    uint16_t* o16 = (uint16_t*)o;
+#define ATTN_DECODE_MERGED_CASE(DTV, DV)                                                     \
+    if (dt == DTV && D == DV) {                                                             \
+        launch_decode_merged_d<DTV, DV>(q16, k16, v16, o16, lse, o_part, lse_part, counters, \
+                                        Tq, Tk, nqt, nsplit, chunk, causal, c, sign, grid,  \
+                                        stream);                                            \
+        return hipGetLastError();                                                           \
+    }
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_BF16, 64)
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_F16, 64)
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_BF16, 32)
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_F16, 32)
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_BF16, 128)
+    ATTN_DECODE_MERGED_CASE(ATTN_DT_F16, 128)
+#undef ATTN_DECODE_MERGED_CASE
+    return hipErrorInvalidValue;
+}
+
 // Kernels 0..5 are the D = 64 ones, then D = 32 (6..11) and D = 128 (12..17),
 // each group ordered bf16 {causal, full, combine}, f16 {causal, full, combine}.
 template <int D>
@@ -391,6 +549,26 @@ const void* decode_kernel_ptr(int index) {
     if (index < 6) return decode_group_ptr<64>(index);
     if (index < 12) return decode_group_ptr<32>(index - 6);
     if (index < 18) return decode_group_ptr<128>(index - 12);
+    return nullptr;
+}
+
+// The merged kernels: D = 64, 32, 128, each bf16 {causal, full}, f16 {causal, full}.
+template <int D>
+static const void* decode_merged_group_ptr(int index) {
+    switch (index) {
+        case 0: return (const void*)decode_split16<ATTN_DT_BF16, true, D, true>;
+        case 1: return (const void*)decode_split16<ATTN_DT_BF16, false, D, true>;
+        case 2: return (const void*)decode_split16<ATTN_DT_F16, true, D, true>;
+        case 3: return (const void*)decode_split16<ATTN_DT_F16, false, D, true>;
+        default: return nullptr;
+    }
+}
+
+const void* decode_merged_kernel_ptr(int index) {
+    if (index < 0) return nullptr;
+    if (index < 4) return decode_merged_group_ptr<64>(index);
+    if (index < 8) return decode_merged_group_ptr<32>(index - 4);
+    if (index < 12) return decode_merged_group_ptr<128>(index - 8);
     return nullptr;
 }
 

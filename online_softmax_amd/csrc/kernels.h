@@ -50,6 +50,20 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
                          float* o_part, float* lse_part, int BH, int Tq, int Tk, int D,
                          int causal, float c, bool negate_q, int dt, hipStream_t stream);
 
+// Decode without allocation: the same split, with the partials in the
+// library's static scratch and the merge done by the last workgroup of each
+// query tile (one launch). The scratch holds kDecodeCounters tile counters
+// and up to kDecodePartRows (row, split) partials of D <= 128.
+constexpr int kDecodeCounters = 256;
+constexpr size_t kDecodeCounterBytes = 1024;
+constexpr size_t kDecodePartRows = 8192;
+constexpr size_t kDecodeScratchBytes = kDecodeCounterBytes + kDecodePartRows * (128 + 1) * 4;
+// Scratch bytes a call needs (0: the sizes do not fit its tile counters).
+size_t decode_scratch_need(int BH, int Tq, int Tk, int D);
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int BH, int Tq, int Tk, int D, int causal,
+                                 float c, bool negate_q, int dt, hipStream_t stream);
+
 // Fused forward for head dimensions 32 and 128 (16-bit dtypes only).
 hipError_t launch_fused_hd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int BH, int T, int D, int causal, float c, bool negate_q, int dt,
@@ -68,6 +82,7 @@ constexpr int kHdKernels = 8;
 constexpr int kRecurrenceKernels = 16;
 constexpr int kBwdAtomicKernels = 8;
 constexpr int kDecodeHdKernels = 12;  // decode at D = 32 and 128 (decode_kernel_ptr 6 .. 17)
+constexpr int kDecodeMergedKernels = 12;  // decode without allocation, D = 64, 32, 128
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
@@ -75,5 +90,6 @@ const void* decode_kernel_ptr(int index);  // 0 .. 5 at D = 64, then D = 32, 128
 const void* hd_kernel_ptr(int index);
 const void* recurrence_kernel_ptr(int index);
 const void* bwd_atomic_kernel_ptr(int index);
+const void* decode_merged_kernel_ptr(int index);
 
 }  // namespace attn

@@ -157,6 +157,23 @@ def test_decode_rejects_invalid(lib, kw, status):
     assert dec(lib, **kw) == status
 
 
+def dec_noalloc(lib, q=FAKE, lse=FAKE, B=1, H=1, Tq=1, Tk=8, D=64, dtype=1, scale=0.125):
+    return lib.attn_decode_noalloc_stream(q, FAKE, FAKE, FAKE, lse, B, H, Tq, Tk, D, 1,
+                                          scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(Tq=0), -1), (dict(Tk=0), -1),
+    (dict(Tq=9, Tk=8), -1), (dict(B=0), -1), (dict(D=96), -2), (dict(D=16), -2),
+    (dict(dtype=0), -2), (dict(dtype=9), -1), (dict(scale=math.inf), -1),
+    (dict(q=FAKE + 8), -1), (dict(lse=FAKE + 2), -1),
+    (dict(Tk=1 << 25), -2),  # one cache slice over 4 GiB
+])
+def test_decode_noalloc_rejects_invalid(lib, kw, status):
+    """Every check runs before the first HIP call (none reaches the device)."""
+    assert dec_noalloc(lib, **kw) == status
+
+
 def rec(lib, q=FAKE, y=FAKE, B=1, T=8, H=1, D=24):
     return lib.attn_gated_recurrence_stream(q, FAKE, FAKE, FAKE, y, B, T, H, D, None)
 
@@ -296,7 +313,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 71
+    assert n == 83
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None
