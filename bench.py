@@ -389,6 +389,43 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, D=64, dtype="bf16",
                 "pass": True})
     log(f"decode D={D}: median {med * 1e3:.1f} us (mean {mean * 1e3:.1f}), {achieved:.0f} GB/s = "
         f"{100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s")
+    # the same calls through the entry point that allocates nothing (one
+    # launch: the last workgroup of each tile merges the split partials),
+    # checked against the workspace entry point's output first
+    o2 = torch.empty_like(qd)
+    lse2 = torch.empty_like(lse)
+    osa.attn_decode_stream(qd, kv[0][0], kv[0][1], o, lse, ws, True, scale, stream)
+    osa.attn_decode_noalloc_stream(qd, kv[0][0], kv[0][1], o2, lse2, True, scale, stream)
+    torch.cuda.synchronize()
+    d_o = float((o2.float() - o.float()).abs().max())
+    d_l = float((lse2 - lse).abs().max())
+    na = {"entry": "attn_decode_noalloc_stream", "kernels": ["decode_merged16"],
+          "vs_workspace_entry": {"max_abs_d_o": d_o, "max_abs_d_lse": d_l},
+          "pass": d_o <= BF16_TOL and d_l <= BF16_TOL}
+    if na["pass"]:
+        for i in range(3 * copies):
+            k, v = kv[i % copies]
+            osa.attn_decode_noalloc_stream(qd, k, v, o2, lse2, True, scale, stream)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            k, v = kv[i % copies]
+            a.record(stream)
+            osa.attn_decode_noalloc_stream(qd, k, v, o2, lse2, True, scale, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms2 = [a.elapsed_time(b) for a, b in ev]
+        med2 = statistics.median(ms2)
+        ach2 = algo / (med2 * 1e-3) / 1e9
+        na.update({"ms": {"mean": statistics.fmean(ms2), "median": med2, "min": min(ms2)},
+                   "roofline": {"bound": "hbm", "achieved": ach2, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": ach2 / PEAK_HBM_GBS}})
+        log(f"decode D={D} without allocation (one launch): median {med2 * 1e3:.1f} us, "
+            f"{ach2:.0f} GB/s = {100 * ach2 / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s")
+    else:
+        log(f"decode D={D} without allocation: differs from the workspace entry point "
+            f"({d_o:.3e}, {d_l:.3e}); not timed")
+    out["noalloc"] = na
+    del o2, lse2
     del kv, qd, o, lse, ws
     return out
 
@@ -900,6 +937,7 @@ def main():
         "memory_beyond_inputs_B": None if mem is None else
             {p: m["held_beyond_inputs_B"] for p, m in mem.items()},
         "legs": {"bwd": leg(bwd), "bwd_atomic": leg(bwd_atomic), "decode": leg(dec),
+                 "decode_noalloc": leg((dec or {}).get("noalloc")),
                  "decode_d128": leg(dec128),
                  "d32": leg((hds or {}).get("32")), "d128": leg((hds or {}).get("128")),
                  "recurrence": leg((recur or {}).get("throughput"))},

@@ -19,7 +19,7 @@
 //  - Q fragments live in VGPRs for the whole kernel.
 //  - 16-bit K and V tiles go straight from HBM to LDS by direct buffer loads
 //    (buffer_load_dwordx4 ... lds) into XOR-swizzled rings of their own, K
-//    four tiles deep and issued three ahead, V three deep and one ahead;
+//    four tiles deep and issued three ahead, V four deep and two ahead;
 //    one barrier per tile. V^T fragments come from transposing LDS reads
 //    (ds_read_b64_tr_b16), so V is stored as it arrives.
 //  - S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}
@@ -216,7 +216,7 @@ __device__ inline void lazy_check(const char* __restrict__ kb,
 // none of which waits for this iteration's vector work; the lazy check of
 // tile j closes the iteration. The (at most two) edge tiles run one at a time
 // with masks. K and V tiles arrive by direct global -> LDS loads into rings
-// of their own, K three tiles ahead and V one (schedule in fused_layout.h);
+// of their own, K three tiles ahead and V two (schedule in fused_layout.h);
 // K(j) stays resident through iteration j for the rare rescale.
 template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
         __syncthreads();
         issue_batch(j);
         v4u32 vf[2][4], kf[2][4];
-        if (PREV) vfrag16(vring[(j + 2) % kRingV], vf, fa);  // V(j-1)
+        if (PREV) vfrag16(vring[(j + kRingV - 1) % kRingV], vf, fa);  // V(j-1)
         if (NEXT) kfrag16(kring[(j + 1) % kRingK], kf, fa);  // K(j+1)
         __builtin_amdgcn_sched_barrier(0);  // the reads go first
         const float t = weights16<DT>(scur, pcur, st.mc, c);
@@ -370,14 +370,14 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
         else
             pv16<DT>(vf, pb, oacc);
     }
-    // edge tiles (diagonal or ragged; at most two), one at a time
+    // edge tiles (diagonal or ragged; at most two), one at a time; their K and
+    // V tiles were issued by earlier batches
     for (int t = n_main; t < n_tiles; ++t) {
         if (!synced) {
             wait_vmcnt<0>();
             __syncthreads();
         }
         synced = false;
-        issue_batch(t);
         if (!CAUSAL || t * BN <= wq0 + 31) {  // a wave skips tiles it cannot see
             v16f32 s[2];
             v4u32 vf[2][4], pf[4];

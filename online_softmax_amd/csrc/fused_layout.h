@@ -131,24 +131,26 @@ ATTN_HD void dl_src(int w, int i, int l, bool is_v, int* row, int* chunk) {
     *chunk = (slot & 7) ^ (is_v ? swz_v(*row) : swz_k(*row));
 }
 // Load schedule of the 16-bit kernel. K tiles and V tiles have rings of
-// their own: K tile t in stage t % 4, V tile t in stage t % 3. Batch u is
-// what the iteration u issues after its barrier: K(u + 3) and V(u + 1), each
+// their own: K tile t in stage t % 4, V tile t in stage t % 4. Batch u is
+// what the iteration u issues after its barrier: K(u + 3) and V(u + 2), each
 // when it exists (0 <= tile < n); the prologue issues batches -3, -2, -1,
-// i.e. K(0), K(1), then K(2) and V(0). Main iteration j (weights of tile j,
-// S(j+1) = K(j+1) Q^T, O += V(j-1) P(j-1), and in the rare rescale case S(j)
-// again from K(j)) reads K(j), K(j+1) and V(j-1), all in batch j - 2 or
-// older, so before its barrier a wave waits until only batch j - 1 is in
-// flight. The reloads of batch j go to K stage (j+3) % 4 (K(j-1), last read
-// in iteration j - 1) and V stage (j+1) % 3 (V(j-2), read in iteration j-1),
-// both finished by every wave at iteration j's barrier.
+// i.e. K(0), then K(1) and V(0), then K(2) and V(1). Main iteration j
+// (weights of tile j, S(j+1) = K(j+1) Q^T, O += V(j-1) P(j-1), and in the
+// rare rescale case S(j) again from K(j)) reads K(j), K(j+1) and V(j-1), all
+// in batch j - 2 or older, so before its barrier a wave waits until only
+// batch j - 1 is in flight. The reloads of batch j go to K stage (j+3) % 4
+// (K(j-1), last read in iteration j - 1) and V stage (j+2) % 4 (V(j-2), read
+// in iteration j-1), both finished by every wave at iteration j's barrier.
+// The edge tiles that follow (at most two, the last ones) find their K and V
+// loaded: their batches are empty.
 ATTN_HD int batch_k(int u, int n) { return (u + 3 >= 0 && u + 3 < n) ? u + 3 : -1; }
-ATTN_HD int batch_v(int u, int n) { return (u + 1 >= 0 && u + 1 < n) ? u + 1 : -1; }
+ATTN_HD int batch_v(int u, int n) { return (u + 2 >= 0 && u + 2 < n) ? u + 2 : -1; }
 // load instructions per wave in batch u (2 per K or V tile)
 ATTN_HD int batch_size(int u, int n) {
     return 2 * (batch_k(u, n) >= 0) + 2 * (batch_v(u, n) >= 0);
 }
 constexpr int kRingK = 4;
-constexpr int kRingV = 3;
+constexpr int kRingV = 4;
 
 // K fragment of S^T tile nt, step ks for lane (ql, h): 16 bytes, dims
 // 16ks + 8h .. +7 of key 32nt + ql.

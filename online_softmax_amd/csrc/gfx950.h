@@ -156,10 +156,12 @@ __device__ inline void wait_lgkmcnt0() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Wait until at most `in_flight` (0, 2, 4 or 6: whole load batches) of this
-// wave's loads are pending.
+// Wait until at most `in_flight` (0, 2, 4, 6 or 8: whole load batches) of
+// this wave's loads are pending.
 __device__ inline void wait_loads(int in_flight) {
-    if (in_flight >= 6)
+    if (in_flight >= 8)
+        wait_vmcnt<8>();
+    else if (in_flight >= 6)
         wait_vmcnt<6>();
     else if (in_flight >= 4)
         wait_vmcnt<4>();
