@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
     int Tq, int Tk, int nqt, int nsplit, int chunk, float c, uint32_t qsign,
     uint16_t* __restrict__ o, float* __restrict__ lse, uint32_t* __restrict__ counters) {
     using G = HeadDim<D>;
+    // ring depth per wave (four stages were measured no faster at D = 64)
     constexpr int kStages = 2;
     constexpr int NI = dec_instr<D>();     // direct loads per K or V tile
     constexpr int NK = G::kSteps, NO = G::kOTiles;
@@ -138,10 +139,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
         for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
     float m = -FLT_MAX, mc = -FLT_MAX * c, l = 0.f;
 
-    // the first two tiles, then the Q rows: the three latencies overlap (the
-    // compiler's wait for Q before its first use also covers the tiles)
-    if (n >= 1) issue(0);
-    if (n >= 2) issue(1);
+    // the Q rows, then the first kStages tiles: the latencies overlap, and
+    // waiting for Q (older than the tiles) waits for no tile
     v4u32 qf[NK];
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
@@ -150,9 +149,19 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
             x = *(const v4u32*)(q + ((int64_t)bh * Tq + my_q) * D + G::q_col(hh, ks));
         qf[ks] = x ^ qsign;
     }
+#pragma unroll
+    for (int st = 0; st < kStages; ++st)
+        if (n > st) issue(st);
     for (int t = 0; t < n; ++t) {
-        if (t + 1 < n)
-            wait_vmcnt<2 * NI>();  // tile t landed, tile t+1 (2 NI loads) in flight
+        // tile t landed; the later tiles already issued (2 NI loads each)
+        // may stay in flight
+        const int ahead = min(kStages - 1, n - 1 - t);
+        if (kStages > 3 && ahead >= 3)
+            wait_vmcnt<(kStages > 3 ? 3 : 0) * 2 * NI>();
+        else if (kStages > 2 && ahead >= 2)
+            wait_vmcnt<(kStages > 2 ? 2 : 0) * 2 * NI>();
+        else if (ahead >= 1)
+            wait_vmcnt<2 * NI>();
         else
             wait_vmcnt<0>();
         const char* kb = ring[wave][t % kStages][0];
@@ -216,9 +225,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
         // the direct loads write the LDS behind the reads' backs, so the
         // reads (issued above, consumed by matrix instructions the compiler
         // may place after this point) are waited for first
-        if (t + 2 < n) {
+        if (t + kStages < n) {
             wait_lgkmcnt0();
-            issue(t + 2);
+            issue(t + kStages);
         }
     }
 
@@ -278,17 +287,25 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void decode_split16(
     if constexpr (MERGED) {
         if (nsplit == 1) return;
         __shared__ int is_last;
-        __threadfence();  // this workgroup's partials, visible device-wide
+        // Every wave's partial stores have completed before the barrier; one
+        // lane then publishes them device-wide with a release on the tile's
+        // counter (one cache write-back per workgroup, not one per wave).
+        wait_vmcnt<0>();
         __syncthreads();
         const int tile = blockIdx.x / nsplit;  // (slice, query tile)
         if (tid == 0) {
-            const uint32_t before = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_ACQ_REL,
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            wait_vmcnt<0>();  // the write-back has completed before the count
+            const uint32_t before = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);
-            is_last = before == (uint32_t)(nsplit - 1);
+            const int last = before == (uint32_t)(nsplit - 1);
+            // only the last workgroup reads the other partials: it alone
+            // acquires (its CU's caches drop what they held of them)
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            is_last = last;
         }
         __syncthreads();
         if (!is_last) return;
-        __threadfence();  // every split's partials before they are read
         if (qrow < Tq) {
             const int64_t row = (int64_t)bh * Tq + qrow;
             const float* lp = lse_part + row * nsplit;
