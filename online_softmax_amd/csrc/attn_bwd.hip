@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv16(
 // qsign negates Q for a negative scale; scale multiplies dQ at the end.
 // ---------------------------------------------------------------------------
 template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_q16(
+__global__ __launch_bounds__(kThreads, 3) void bwd_q16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ ndelta,
@@ -406,6 +406,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
         dl = -ndelta[(int64_t)bh * T + my_q];
     }
     wait_vmcnt<0>();
+    // -delta in every register: the start of each dP^T accumulator, so the
+    // products leave dP - delta with no subtraction per score
+    v16f32 ndl16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
 
     const uint32_t slice_bytes = (uint32_t)T * (kHeadDim * 2);
     const v4u32_rsrc krs = buffer_rsrc(k + base, slice_bytes);
@@ -421,13 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
         load_btile(vrs, voff, u * BN, T, wave_u, (uint32_t)(uintptr_t)(lds_void*)vring[st]);
     };
 
-    uint32_t rb[4], tb[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) rb[ks] = (uint32_t)bfrag_byte(ql, hh, 0, ks);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) tb[ct][half] = (uint32_t)btr_byte(lane, ct, 0, half);
+    const uint32_t rb0 = (uint32_t)bfrag_byte(ql, hh, 0, 0);
+    const uint32_t tb00 = (uint32_t)btr_byte(lane, 0, 0, 0);
 
     v16f32 dqt[2];
 #pragma unroll
@@ -440,9 +440,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
     // halves, dP^T, packed dS^T of one, their fragments) fits beside the
     // accumulators at two workgroups per CU.
     // Row fragments (A operands) of half nt of a K or V tile.
+    // (step ks's lane base is step 0's with bits 5-6 flipped by ks: the
+    // swizzle permutes 32-byte pairs within a row, and ring stages are
+    // 1024-aligned, so the flip commutes with adding the stage)
     auto rows4 = [&](const char* tile, int nt, v4u32(&f)[4]) {
+        const uint32_t a0 = (uint32_t)(uintptr_t)lane_tile(tile, rb0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) f[ks] = brow_at(lane_tile(tile, rb[ks]), nt);
+        for (int ks = 0; ks < 4; ++ks)
+            f[ks] = brow_at((const lds_char*)(uintptr_t)(a0 ^ ((uint32_t)ks << 5)), nt);
     };
     // acc = X B for 4 steps (X fragments f, B the lane's Q or dO row)
     auto prod4 = [&](const v4u32(&f)[4], const v4u32(&bf)[4], v16f32& acc) {
@@ -472,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
                         const int key = k0 + acc_row(r, hh);
                         p = (key < T && (!CAUSAL || key <= my_q)) ? p : 0.f;
                     }
-                    d[e] = p * (dp[r] - dl);
+                    d[e] = p * dp[r];
                 }
                 sf[kl][i] = pack2<DT>(d[0], d[1]);
             }
@@ -494,8 +499,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
     auto half = [&](int u, int nt, v16f32& scur, v16f32& snext, auto next_tag, auto edge_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
         const int st = u % kStages;
+        // the V fragments, then (once the dP products hold them) the K
+        // fragments of the next half: the two sets are never live together
         v4u32 fd[4], fs[4];
         rows4(vring[st], nt, fd);
+        __builtin_amdgcn_sched_barrier(0);
+        v16f32 dp = ndl16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dp = mfma16<DT>(fd[ks], of[ks], dp);
         if (NEXT) {
             if (nt == 0)
                 rows4(kring[st], 1, fs);
@@ -503,17 +514,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q16(
                 rows4(kring[(u + 1) % kStages], 0, fs);
         }
         __builtin_amdgcn_sched_barrier(0);
-        v16f32 dp;
         v4u32 sf[2];
-        prod4(fd, of, dp);
         if (NEXT) prod4(fs, qf, snext);
         make_ds(u, nt, scur, dp, sf, edge_tag);
         __builtin_amdgcn_sched_barrier(0);
+        // lane bases of the transposed reads from the one of (ct 0, half 0):
+        // column block ct flips address bit 6, half 1 flips bit 5 and adds
+        // 8 rows (the 1024 rides in the read's offset)
         const lds_char* ktr[2][2];
+        const uint32_t t00 = (uint32_t)(uintptr_t)lane_tile(kring[st], tb00);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) ktr[ct][hf] = lane_tile(kring[st], tb[ct][hf]);
+            for (int hf = 0; hf < 2; ++hf)
+                ktr[ct][hf] = (const lds_char*)(uintptr_t)(t00 ^ ((uint32_t)ct << 6) ^
+                                                             ((uint32_t)hf << 5)) +
+                              1024 * hf;
 #pragma unroll
         for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
