@@ -887,8 +887,8 @@ def main():
     if oracle is not None:
         single = oracle_single_core(oracle)
 
-    kname = osa.attn_kernel_name({"bf16": 0, "f16": 2, "f32": 4}[w.dtype] +
-                                 (0 if w.causal else 1))
+    dt_code = {"f32": osa.ATTN_F32, "bf16": osa.ATTN_BF16, "f16": osa.ATTN_F16}[w.dtype]
+    kname = osa.attn_kernel_name(osa.attn_fused_kernel(w.B, w.H, w.T, w.D, w.causal, dt_code))
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": measured_traffic(), "kernel": kname,
                 "launch_ms": {"mean": t["mean"], "median": t["median"]}}

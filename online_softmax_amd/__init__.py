@@ -12,7 +12,7 @@ from .binding import (  # noqa: F401
     AttnError, attention, attention_backward, attention_decode, attn_bwd_flops,
     attn_bwd_stream, attn_bwd_atomic_stream, attn_bwd_atomic_workspace_bytes,
     attn_decode_stream, attn_decode_workspace_bytes, attn_decode_noalloc_stream,
-    attn_bwd_workspace_bytes, attn_flops, attn_fused_tile, attn_fwd,
+    attn_bwd_workspace_bytes, attn_flops, attn_fused_tile, attn_fused_kernel, attn_fwd,
     attn_fwd_stream, attn_kernel_attributes, attn_kernel_count,
     attn_kernel_name, attn_last_hip_error, attn_naive_fwd,
     attn_naive_workspace_bytes, attn_status_string, attn_traffic_bytes,

@@ -30,7 +30,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_naive_fwd",
            "attn_flops", "attn_status_string", "attn_last_hip_error",
            "attn_kernel_count", "attn_kernel_name", "attn_kernel_attributes",
            "attn_fused_tile", "attn_gated_recurrence_stream",
-           "attn_gated_recurrence_flops", "attn_decode_noalloc_stream")
+           "attn_gated_recurrence_flops", "attn_decode_noalloc_stream",
+           "attn_fused_kernel")
 
 
 class AttnError(RuntimeError):
@@ -104,6 +105,7 @@ def load(path: str = LIBRARY):
         lib.attn_kernel_name.restype = ctypes.c_char_p
         lib.attn_kernel_attributes.argtypes = [I, ctypes.POINTER(attn_kernel_attr)]
         lib.attn_fused_tile.argtypes = [I, ctypes.POINTER(I), ctypes.POINTER(I)]
+        lib.attn_fused_kernel.argtypes = [I, I, I, I, I, I]
         for name in EXPORTS:  # fail here, not at first use, if one is absent
             getattr(lib, name)
         if path == LIBRARY:
@@ -356,6 +358,14 @@ def attn_fused_tile(dtype: int):
     _check(_lib().attn_fused_tile(dtype, ctypes.byref(bm), ctypes.byref(bn)),
            "attn_fused_tile")
     return bm.value, bn.value
+
+
+def attn_fused_kernel(B: int, H: int, T: int, D: int, causal: bool, dtype: int) -> int:
+    """Kernel-table index of the kernel attn_fwd launches for these
+    arguments (see attn_kernel_name)."""
+    r = int(_lib().attn_fused_kernel(B, H, T, D, int(bool(causal)), dtype))
+    _check(r if r < 0 else ATTN_OK, "attn_fused_kernel")
+    return r
 
 
 def attn_status_string(status: int) -> str:

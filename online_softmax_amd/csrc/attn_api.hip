@@ -371,6 +371,27 @@ int attn_fused_tile(int dtype, int* block_m, int* block_n) {
     return ATTN_OK;
 }
 
+int attn_fused_kernel(int B, int H, int T, int D, int causal, int dtype) {
+    if (!valid_dtype(dtype)) return ATTN_ERR_INVALID;
+    const int st = check_shape(B, H, T, D,
+                               dtype == ATTN_F32 ? D == attn::kHeadDim : fwd16_head_dim(D));
+    if (st != ATTN_OK) return st;
+    // kernel table order (attn_kernel_name): fused 16-bit / fp32 first,
+    // the head-dimension kernels after the decode ones, the eight-wave
+    // kernels last; within each group bf16 before f16, causal before full
+    const int full = causal ? 0 : 1, f16 = dtype == ATTN_F16 ? 2 : 0;
+    const long long bh = (long long)B * H;
+    if (dtype == ATTN_F32) return (attn::fwd32_split(bh, T) ? 6 : 4) + full;
+    if (D != attn::kHeadDim) {
+        const int hd0 = attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
+                        attn::kDecodeKernels;
+        return hd0 + (D == 128 ? 4 : 0) + f16 + full;
+    }
+    if (attn::fwd16_eight_waves(bh, T))
+        return attn_kernel_count() - attn::kFwdW8Kernels + f16 + full;
+    return f16 + full;
+}
+
 int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
                        int causal, attn_traffic* out) {
     if (!out) return ATTN_ERR_INVALID;
@@ -394,8 +415,11 @@ int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
         // K and V rows each query tile loads (rows >= T are never fetched)
         int bm, bn;
         attn_fused_tile(dtype, &bm, &bn);
-        // fp32 on a small grid runs the key-split kernel on 32-row tiles
+        // fp32 on a small grid runs the key-split kernel on 32-row tiles;
+        // 16-bit D = 64 on a large one the eight-wave kernel on 256-row tiles
         if (dtype == ATTN_F32 && attn::fwd32_split((long long)bh, T)) bm = attn::kSplitRows;
+        if (dtype != ATTN_F32 && D == attn::kHeadDim && attn::fwd16_eight_waves((long long)bh, T))
+            bm = attn::kBlockM8;
         const int nq = (T + bm - 1) / bm;
         uint64_t kv_rows = 0;
         for (int qt = 0; qt < nq; ++qt) {
@@ -440,7 +464,8 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 int attn_kernel_count(void) {
     return attn::kFusedKernels + attn::kNaiveKernels + attn::kBwdKernels +
            attn::kDecodeKernels + attn::kHdKernels + attn::kRecurrenceKernels +
-           attn::kBwdAtomicKernels + attn::kDecodeHdKernels + attn::kDecodeMergedKernels;
+           attn::kBwdAtomicKernels + attn::kDecodeHdKernels + attn::kDecodeMergedKernels +
+           attn::kFwdW8Kernels;
 }
 
 const char* attn_kernel_name(int kernel) {
@@ -486,7 +511,9 @@ const char* attn_kernel_name(int kernel) {
         "decode_merged16<bf16, causal, 32>", "decode_merged16<bf16, full, 32>",
         "decode_merged16<f16, causal, 32>", "decode_merged16<f16, full, 32>",
         "decode_merged16<bf16, causal, 128>", "decode_merged16<bf16, full, 128>",
-        "decode_merged16<f16, causal, 128>", "decode_merged16<f16, full, 128>"};
+        "decode_merged16<f16, causal, 128>", "decode_merged16<f16, full, 128>",
+        "fused_fwd16w8<bf16, causal>", "fused_fwd16w8<bf16, full>",
+        "fused_fwd16w8<f16, causal>",  "fused_fwd16w8<f16, full>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }
@@ -500,7 +527,9 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     const int bat0 = rec0 + attn::kRecurrenceKernels;
     const int dhd0 = bat0 + attn::kBwdAtomicKernels;
     const int dmg0 = dhd0 + attn::kDecodeHdKernels;
-    const void* fn = kernel < naive0  ? attn::fused_kernel_ptr(kernel)
+    const int w80 = dmg0 + attn::kDecodeMergedKernels;
+    const void* fn = kernel >= w80    ? attn::fused_w8_kernel_ptr(kernel - w80)
+                     : kernel < naive0  ? attn::fused_kernel_ptr(kernel)
                      : kernel < bwd0 ? attn::naive_kernel_ptr(kernel - naive0)
                      : kernel < dec0 ? attn::bwd_kernel_ptr(kernel - bwd0)
                      : kernel < hd0  ? attn::decode_kernel_ptr(kernel - dec0)
@@ -514,7 +543,8 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out) {
     if (e != hipSuccess) return hip_fail(e);
     // threads per workgroup of the kernel's launches: the recurrence's
     // kernel i runs i + 1 waves
-    const int threads = kernel >= 6 && kernel < naive0 ? attn::kSplitThreads
+    const int threads = kernel >= w80 ? attn::kThreads8
+                        : kernel >= 6 && kernel < naive0 ? attn::kSplitThreads
                         : kernel >= bat0     ? attn::kThreads
                         : kernel >= rec0 + 8 ? 64
                         : kernel >= rec0   ? 64 * (kernel - rec0 + 1)

@@ -408,6 +408,195 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
 }
 
 // ---------------------------------------------------------------------------
+// 8 waves, 32 query rows each (256 per workgroup), sharing every K and V
+// tile: each wave fetches one eighth of a tile (one 1 KiB direct load per
+// ring), so a tile's loads and its LDS writes serve twice the rows of the
+// 4-wave kernel. The loop is plain (S, weights, P.V of one tile at a time,
+// the lazy reference of softmax_tile), which keeps a wave within 128 VGPRs:
+// two workgroups then give every SIMD four waves, and the SIMD interleaves
+// one wave's matrix instructions with another's vector work instead of the
+// kernel pipelining them inside one wave. Rings: K and V four tiles deep,
+// tile t + 3 issued after the barrier of iteration t into the stage tile
+// t - 1 used. Each wave computes only its own tiles (w8_seen) and masks only
+// its own diagonal and the ragged tile (w8_main); it joins every barrier.
+// ---------------------------------------------------------------------------
+template <int DT, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
+    constexpr int BN = kBlockN16;
+    __shared__ __attribute__((aligned(1024))) char kring[kRing8][kTileBytes16];
+    __shared__ __attribute__((aligned(1024))) char vring[kRing8][kTileBytes16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ql = lane & 31;
+    const int hh = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
+
+    int bh, qt;
+    tile_of8(blockIdx.x, gridDim.x, nq, CAUSAL, &bh, &qt);
+    const int64_t base = (int64_t)bh * T * kHeadDim;
+    const int wq0 = qt * kBlockM8 + 32 * wave_u;  // first query row of this wave
+    const int my_q = wq0 + ql;                    // this lane's query row
+    const int n_tiles = key_tiles(qt, T, BN, CAUSAL, kBlockM8);
+    const int n_seen = w8_seen(qt, wave_u, T, CAUSAL);
+
+    // Q rows first: their loads are older than every ring load, so the
+    // first tile's wait covers them too
+    v4u32 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        v4u32 x = {0u, 0u, 0u, 0u};
+        if (my_q < T)
+            x = *(const v4u32*)(q + base + (int64_t)my_q * kHeadDim + q_col16(hh, ks));
+        qf[ks] = x ^ qsign;
+    }
+
+    // wave w's share of a tile: the 4-wave schedule's instruction w (rows
+    // 8w .. 8w + 7); the ragged last tile clamps rows past T to row T - 1
+    // (their weights are masked to 0), and the slice's buffer bounds every
+    // access in any case
+    const uint32_t slice_bytes = (uint32_t)T * (kHeadDim * 2);
+    const v4u32_rsrc krs = buffer_rsrc(k + base, slice_bytes);
+    const v4u32_rsrc vrs = buffer_rsrc(v + base, slice_bytes);
+    const uint32_t kvoff = (uint32_t)dl_global_byte(wave >> 1, wave & 1, lane, false);
+    const uint32_t vvoff = (uint32_t)dl_global_byte(wave >> 1, wave & 1, lane, true);
+    auto load_tile = [&](v4u32_rsrc rs, const char* stage, uint32_t voff, int tile) {
+        const uint32_t off = (uint32_t)(uintptr_t)(lds_void*)stage + 1024 * wave_u;
+        const int k0 = tile * BN;
+        if (k0 + BN <= T) {
+            dma16(rs, voff, (uint32_t)k0 * (kHeadDim * 2), off);
+        } else {
+            const int r = min(k0 + (int)(voff >> 7), T - 1);
+            dma16(rs, (uint32_t)r * (kHeadDim * 2) + (voff & 127), 0u, off);
+        }
+    };
+    auto issue = [&](int t) {
+        load_tile(krs, kring[t % kRing8], kvoff, t);
+        load_tile(vrs, vring[t % kRing8], vvoff, t);
+    };
+    for (int t = 0; t < kAhead8 && t < n_tiles; ++t) issue(t);
+
+    // Fragment addresses from one lane base per tile each: the swizzles only
+    // permute 16-byte chunks within a row and the stages are 8 KiB aligned,
+    // so K step ks is base XOR (ks << 5) (the second key half adds 4096) and
+    // V output block mt is base XOR (mt << 6) (steps and halves add
+    // constants), checked on the host for every lane and stage.
+    const uint32_t ko0 = (uint32_t)kfrag_byte(ql, hh, 0, 0);
+    const uint32_t vo0 = (uint32_t)vtr_byte(lane, 0, 0, 0);
+
+    v16f32 oacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
+    // reference max starts finite (-FLT_MAX): no inf - inf, and scale 0 works
+    RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
+
+    // One tile. The fragment reads go in groups of four (16 registers),
+    // fenced from the scheduler, so a wave stays within 128 VGPRs: the LDS
+    // latency a wave then waits out is covered by the SIMD's other waves.
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) v4u32 lds_v4u32;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    auto step = [&](int t, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        uint32_t ka = (uint32_t)(uintptr_t)(lds_void*)kring[t % kRing8] + ko0;
+        uint32_t va = (uint32_t)(uintptr_t)(lds_void*)vring[t % kRing8] + vo0;
+        asm("" : "+v"(ka), "+v"(va));  // one address each; constants ride in offsets
+        v16f32 s[2];
+        v4u32 f[4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                f[ks] = *(const lds_v4u32*)((const lds_char*)(uintptr_t)(ka ^ ((uint32_t)ks << 5)) +
+                                            kKfragNtStride * nt);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s[nt] = mfma16<DT>(f[ks], qf[ks], s[nt]);
+        }
+        v4u32 pf[4];
+        softmax_tile<DT, CAUSAL, EDGE, 2>(s, pf, oacc, st, c, t * BN, T, my_q, hh);
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ks = 2 * kp + (j >> 1), mt = j & 1;
+                const lds_char* p =
+                    (const lds_char*)(uintptr_t)(va ^ ((uint32_t)mt << 6)) + kVtrKsStride * ks;
+                const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+                const v4i16 b =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + kVtrHalfStride));
+                const v2u32 a2 = __builtin_bit_cast(v2u32, a), b2 = __builtin_bit_cast(v2u32, b);
+                f[j] = (v4u32){a2[0], a2[1], b2[0], b2[1]};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ks = 2 * kp + (j >> 1), mt = j & 1;
+                oacc[mt] = mfma16<DT>(f[j], pf[ks], oacc[mt]);
+            }
+        }
+    };
+    auto sync_issue = [&](int t) {
+        // this wave's loads of tile t (and the Q rows) have landed; those of
+        // the (up to two) later tiles already issued may still be in flight
+        const int ahead = min(kAhead8 - 1, n_tiles - 1 - t);
+        if (ahead >= 2)
+            wait_vmcnt<4>();
+        else if (ahead == 1)
+            wait_vmcnt<2>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // everyone's share landed; tile t - 1's stages are free
+        if (t + kAhead8 < n_tiles) issue(t + kAhead8);
+    };
+    // Tiles every wave computes unmasked (those before the first wave's
+    // first masked one), then the last few (at most four), where each wave
+    // takes the masked step on every tile it sees: on a tile that needs no
+    // mask it masks nothing and takes the same decisions, so the results
+    // are the same bits, and one step form keeps the tail within the
+    // register budget.
+    const int n_all_main = w8_main(qt, 0, T, CAUSAL);
+    int t = 0;
+    for (; t < n_all_main; ++t) {
+        sync_issue(t);
+        if (t < n_seen) step(t, std::integral_constant<bool, false>());  // rows < T
+    }
+    for (; t < n_tiles; ++t) {
+        sync_issue(t);
+        if (t < n_seen) step(t, std::integral_constant<bool, true>());
+    }
+
+    // the output row from an opaque copy of the thread index, so its address
+    // is not computed before the loop and carried through it
+    int tid_late = tid;
+    asm("" : "+v"(tid_late));
+    const int row = qt * kBlockM8 + 32 * (tid_late >> 6) + (tid_late & 31);
+    const float lt = halves_sum(st.l);
+    const float inv = 1.0f / lt;
+    if (row < T) {
+        uint16_t* orow = o + base + (int64_t)row * kHeadDim;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                v2u32 w;
+                w[0] = pack2<DT>(oacc[mt][4 * g] * inv, oacc[mt][4 * g + 1] * inv);
+                w[1] = pack2<DT>(oacc[mt][4 * g + 2] * inv,
+                                 oacc[mt][4 * g + 3] * inv);
+                *(v2u32*)(orow + 32 * mt + acc_row(4 * g, hh)) = w;
+            }
+        if (lse != nullptr && (tid_late & 32) == 0)
+            lse[(int64_t)bh * T + row] = (st.mc + log2f(lt)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs: the same schedule on v_mfma_f32_32x32x2_f32, 32-key tiles,
 // fp32 weights (no lazy path: this kernel is bound by the fp32 matrix rate).
 // qsign = 0x80000000 negates Q for a negative scale.
@@ -774,6 +963,16 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, void* o,
                                (const float*)q, (const float*)k, (const float*)v, (float*)o,
                                lse, T, nq, c, sign);
         }
+    } else if (fwd16_eight_waves(BH, T)) {
+        const int nq = (T + kBlockM8 - 1) / kBlockM8;
+        const dim3 grid((unsigned)(nq * BH));
+        const dim3 block(kThreads8);
+        const uint32_t sign = negate_q ? 0x80008000u : 0u;
+        auto fn = dt == ATTN_DT_BF16
+                      ? (causal ? fused_fwd16w8<ATTN_DT_BF16, true> : fused_fwd16w8<ATTN_DT_BF16, false>)
+                      : (causal ? fused_fwd16w8<ATTN_DT_F16, true> : fused_fwd16w8<ATTN_DT_F16, false>);
+        hipLaunchKernelGGL(fn, grid, block, 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+                           (const uint16_t*)v, (uint16_t*)o, lse, T, nq, c, sign);
     } else {
         const int nq = (T + kBlockM - 1) / kBlockM;
         const dim3 grid((unsigned)(nq * BH));
@@ -806,6 +1005,16 @@ const void* fused_kernel_ptr(int index) {
         case 5: return (const void*)fused_fwd32<false>;
         case 6: return (const void*)fused_fwd32_split<true>;
         case 7: return (const void*)fused_fwd32_split<false>;
+        default: return nullptr;
+    }
+}
+
+const void* fused_w8_kernel_ptr(int index) {
+    switch (index) {
+        case 0: return (const void*)fused_fwd16w8<ATTN_DT_BF16, true>;
+        case 1: return (const void*)fused_fwd16w8<ATTN_DT_BF16, false>;
+        case 2: return (const void*)fused_fwd16w8<ATTN_DT_F16, true>;
+        case 3: return (const void*)fused_fwd16w8<ATTN_DT_F16, false>;
         default: return nullptr;
     }
 }

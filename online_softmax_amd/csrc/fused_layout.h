@@ -186,6 +186,69 @@ ATTN_HD int dl_global_byte(int w, int i, int l, bool is_v) {
     return row * kHeadDim * 2 + chunk * 16;
 }
 
+// ---- 16-bit forward, eight-wave workgroups (D = 64) --------------------------
+// kWaves8 wave64s own 32 query rows each (kBlockM8 = 256 per workgroup) and
+// share every K and V tile: one 1 KiB direct load per wave per tile (wave w
+// is the 4-wave schedule's instruction w: tile rows 8w .. 8w + 7), K tile t
+// in stage t % kRing8 of its ring, V likewise, tiles issued kAhead8 ahead.
+// Each wave runs the plain loop (S, weights, P.V of one tile at a time); at
+// <= 128 VGPRs two workgroups put four waves on every SIMD, whose matrix and
+// vector work the hardware interleaves.
+constexpr int kWaves8 = 8;
+constexpr int kThreads8 = 64 * kWaves8;
+constexpr int kBlockM8 = 32 * kWaves8;
+constexpr int kRing8 = 4;
+constexpr int kAhead8 = kRing8 - 1;
+// Tiles of query tile qt that wave w computes (a key visible to one of its
+// valid rows), and how many leading ones need no mask (every key < T and,
+// causal, <= the wave's first row). The wave's tiles between the two (at
+// most its diagonal tile and the ragged last tile) take the masked step.
+// A wave whose rows all lie past T computes none.
+ATTN_HD int w8_seen(int qt, int w, int T, bool causal) {
+    const int wq0 = qt * kBlockM8 + 32 * w;
+    if (wq0 >= T) return 0;
+    const int all = (T + kBlockN16 - 1) / kBlockN16;
+    if (!causal) return all;
+    const int last = wq0 + 31 < T - 1 ? wq0 + 31 : T - 1;
+    const int n = last / kBlockN16 + 1;
+    return n < all ? n : all;
+}
+ATTN_HD int w8_main(int qt, int w, int T, bool causal) {
+    const int wq0 = qt * kBlockM8 + 32 * w;
+    if (wq0 >= T) return 0;
+    int n = T / kBlockN16;
+    if (causal) {
+        const int c = (wq0 + 1) / kBlockN16;
+        if (c < n) n = c;
+    }
+    const int seen = w8_seen(qt, w, T, causal);
+    return n < seen ? n : seen;
+}
+// Workgroup -> (slice, 256-row query tile) of the eight-wave kernel. As in
+// tile_of, each XCD keeps whole slices (their K and V stay in its L2), but
+// within an XCD the order is query tile major: the heaviest causal tiles
+// of all its slices first, then the next ones. With 256-row tiles a slice
+// has half as many tiles of twice the work, and walking slice by slice
+// leaves the last heavy tiles of the last slice to run alone at the end.
+ATTN_HD void tile_of8(int block, int total, int nq, bool causal, int* bh, int* qt) {
+    const int BH = total / nq;
+    if ((total & 7) != 0 || (BH & 7) != 0) {
+        tile_of(block, total, nq, causal, bh, qt);
+        return;
+    }
+    const int spx = BH >> 3;  // slices per XCD
+    const int x = block & 7, i = block >> 3;
+    *bh = x * spx + i % spx;
+    const int t = i / spx;
+    *qt = causal ? nq - 1 - t : t;
+}
+// The eight-wave kernel runs when its grid has at least one workgroup per
+// CU; shorter calls keep the 128-row kernel, whose grid is twice as large.
+constexpr int kW8MinGrid = 256;
+ATTN_HD bool fwd16_eight_waves(long long BH, int T) {
+    return (long long)((T + kBlockM8 - 1) / kBlockM8) * BH >= kW8MinGrid;
+}
+
 // ---- other head dimensions (16-bit forward, D = 32 or 128) -----------------
 // Tiles of 64 keys x D dims, rows of 2D bytes (C = D / 8 chunks of 16 B),
 // filled by direct loads of 1 KiB wave instructions (D / 8 per tile, D / 32

@@ -83,6 +83,7 @@ constexpr int kRecurrenceKernels = 16;
 constexpr int kBwdAtomicKernels = 8;
 constexpr int kDecodeHdKernels = 12;  // decode at D = 32 and 128 (decode_kernel_ptr 6 .. 17)
 constexpr int kDecodeMergedKernels = 12;  // decode without allocation, D = 64, 32, 128
+constexpr int kFwdW8Kernels = 4;          // 8-wave 16-bit forward, D = 64
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);
@@ -91,5 +92,6 @@ const void* hd_kernel_ptr(int index);
 const void* recurrence_kernel_ptr(int index);
 const void* bwd_atomic_kernel_ptr(int index);
 const void* decode_merged_kernel_ptr(int index);
+const void* fused_w8_kernel_ptr(int index);
 
 }  // namespace attn

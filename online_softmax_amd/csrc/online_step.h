@@ -98,13 +98,17 @@ __device__ inline void softmax_tile(v16f32 (&s)[2], v4u32 (&pf)[4],
     };
     if (EDGE) {
         pending();
+        // key k0 + 32 nt + acc_row(r, hh) is masked when it is past T - 1 or
+        // (causal) past the row: with lim = min(T - 1, row) - k0 - 4 hh that
+        // is 32 nt + acc_row(r, 0) > lim, a constant against one per-lane
+        // value (no per-register offsets kept live across the loop)
+        int lim = (CAUSAL ? min(T - 1, my_q) : T - 1) - k0 - 4 * hh;
+        asm("" : "+v"(lim));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 32 * nt + acc_row(r, hh);
-                if (key >= T || (CAUSAL && key > my_q)) s[nt][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (32 * nt + acc_row(r, 0) > lim) s[nt][r] = -INFINITY;
         rescale();
         st.l += weights(st.mc);
     } else {

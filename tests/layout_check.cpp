@@ -986,6 +986,83 @@ static void check_ring(int n, int n_main) {
     }
 }
 
+// The eight-wave 16-bit forward: workgroup -> (slice, 256-row query tile)
+// is a bijection; each wave computes exactly the key tiles that hold a key
+// one of its valid rows sees (w8_seen), the tiles before the first wave's
+// masked one need no mask for any wave that computes them, at most four
+// tiles follow them (the per-wave masked tail), and the load schedule's
+// waits and stage reuse hold for every tile count.
+static void check_w8(int BH, int T, bool causal) {
+    const int nq = (T + kBlockM8 - 1) / kBlockM8;
+    const int total = nq * BH;
+    std::vector<int> hit(total, 0);
+    for (int b = 0; b < total; ++b) {
+        int bh, qt;
+        tile_of8(b, total, nq, causal, &bh, &qt);
+        CHECK(bh >= 0 && bh < BH && qt >= 0 && qt < nq, "w8 tile_of8(%d)", b);
+        if ((total & 7) == 0 && (BH & 7) == 0)  // each XCD keeps whole slices
+            CHECK(bh / (BH / 8) == (b & 7), "w8 tile_of8(%d): slice %d off its XCD", b, bh);
+        if (bh >= 0 && bh < BH && qt >= 0 && qt < nq) hit[bh * nq + qt]++;
+    }
+    for (int i = 0; i < total; ++i) CHECK(hit[i] == 1, "w8 tile %d hit %d times", i, hit[i]);
+    for (int qt = 0; qt < nq; ++qt) {
+        const int n_tiles = key_tiles(qt, T, kBlockN16, causal, kBlockM8);
+        const int n_all_main = w8_main(qt, 0, T, causal);
+        CHECK(n_all_main >= 0 && n_all_main <= n_tiles && n_tiles - n_all_main <= 4,
+              "w8 T %d qt %d: %d unmasked of %d tiles", T, qt, n_all_main, n_tiles);
+        CHECK(n_tiles >= 1 && (long)(n_tiles - 1) * kBlockN16 < T, "w8 T %d qt %d: tiles", T, qt);
+        for (int w = 0; w < kWaves8; ++w) {
+            const int wq0 = qt * kBlockM8 + 32 * w;
+            const int rlast = std::min(wq0 + 31, T - 1);
+            const int seen = w8_seen(qt, w, T, causal);
+            CHECK(seen >= 0 && seen <= n_tiles, "w8 T %d qt %d w %d: seen %d of %d", T, qt, w, seen,
+                  n_tiles);
+            const int wm = w8_main(qt, w, T, causal);
+            CHECK(wm >= 0 && wm <= seen, "w8 main %d > seen %d", wm, seen);
+            for (int t = 0; t < n_tiles; ++t) {
+                bool vis = false, needs_mask = false;
+                for (int r = wq0; r <= rlast; ++r)
+                    for (int key = t * kBlockN16; key < (t + 1) * kBlockN16; ++key) {
+                        const bool ok = key < T && (!causal || key <= r);
+                        vis = vis || ok;
+                        needs_mask = needs_mask || !ok;
+                    }
+                CHECK(vis == (t < seen), "w8 T %d qt %d w %d tile %d: visible %d, seen %d", T, qt,
+                      w, t, (int)vis, seen);
+                if (t < n_all_main && t < seen)
+                    CHECK(!needs_mask, "w8 T %d qt %d w %d: unmasked tile %d needs a mask", T, qt,
+                          w, t);
+                if (t < wm) CHECK(!needs_mask, "w8 per-wave main tile %d needs a mask", t);
+            }
+        }
+        // ring: tile t in stage t % kRing8, t + kAhead8 issued after the
+        // barrier of iteration t; the wait leaves the later issued tiles
+        // (2 loads each) pending and needs tile t's loads done
+        for (int t = 0; t < n_tiles; ++t) {
+            const int issued_before = std::min(t + kAhead8 - 1, n_tiles - 1);  // last tile issued
+            const int ahead = std::min(kAhead8 - 1, n_tiles - 1 - t);
+            CHECK(ahead == issued_before - t && ahead >= 0 && ahead <= 2, "w8 ring wait at %d", t);
+            if (t + kAhead8 < n_tiles)
+                CHECK((t + kAhead8) % kRing8 == (t + kRing8 - 1) % kRing8 &&
+                          (t + kAhead8) % kRing8 != t % kRing8,
+                      "w8 ring stage reuse at %d", t);
+        }
+    }
+    // wave w's direct load is the 4-wave schedule's instruction w: it lands
+    // at byte 1024 w of the stage, and the 8 waves cover each tile once
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        std::vector<int> cov(512, 0);
+        for (int w = 0; w < kWaves8; ++w)
+            for (int l = 0; l < 64; ++l) {
+                int row, chunk;
+                dl_src(w >> 1, w & 1, l, is_v, &row, &chunk);
+                CHECK(row == 8 * w + l / 8, "w8 direct load row");
+                cov[row * 8 + chunk]++;
+            }
+        for (int i = 0; i < 512; ++i) CHECK(cov[i] == 1, "w8 direct load coverage %d", i);
+    }
+}
+
 int main() {
     check_direct16();
     check_bwd_layout();
@@ -1056,6 +1133,11 @@ int main() {
             check_key_cover(T, kBlockN32, causal);
         }
     check16(48, 8192, true);
+    for (int T : {1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256, 257, 300, 511,
+                  512, 513, 700, 1000, 1024, 1100, 2048, 4096})
+        for (int BH : {1, 3, 8, 48})
+            for (int causal = 0; causal < 2; ++causal) check_w8(BH, T, causal);
+    for (int causal = 0; causal < 2; ++causal) check_w8(1, 8192, causal);
     if (failures) {
         std::printf("%d failures\n", failures);
         return 1;

@@ -257,6 +257,8 @@ def fused_ask_closed_form(B, H, T, dtype, causal):
     bm, bn = osa.attn_fused_tile(dtype)
     if dtype == osa.ATTN_F32 and -(-T // 128) * B * H < 256:
         bm = 32  # the key-split kernel's 32-row tiles on small grids
+    if dtype != osa.ATTN_F32 and -(-T // 256) * B * H >= 256:
+        bm = 256  # the eight-wave kernel's 256-row tiles on large grids
     elt = 4 if dtype == osa.ATTN_F32 else 2
     nq = -(-T // bm)
     rows = 0
@@ -277,6 +279,29 @@ def test_fused_traffic(dtype, causal, T):
     assert t["score_matrix"] == 0 and t["table_bytes"] == 0
     assert t["ask"] == fused_ask_closed_form(4, 12, T, dtype, causal)
     assert t["ask"] >= t["floor"]
+
+
+def test_fused_kernel_selection():
+    """attn_fused_kernel names the kernel attn_fwd launches: the eight-wave
+    16-bit kernel once its 256-row grid reaches 256 workgroups, the 128-row
+    one below, the fp32 key-split kernel on small fp32 grids, the head-dim
+    kernels for D = 32 / 128; invalid arguments give attn_fwd's status."""
+    name = lambda *a: osa.attn_kernel_name(osa.attn_fused_kernel(*a))
+    assert name(4, 12, 8192, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"
+    assert name(4, 12, 8192, 64, False, osa.ATTN_F16) == "fused_fwd16w8<f16, full>"
+    assert name(4, 12, 2048, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"  # 384
+    assert name(4, 12, 1024, 64, True, osa.ATTN_BF16) == "fused_fwd16<bf16, causal>"    # 192
+    assert name(1, 256, 1, 64, False, osa.ATTN_F16) == "fused_fwd16w8<f16, full>"       # 256
+    assert name(1, 255, 1, 64, False, osa.ATTN_F16) == "fused_fwd16<f16, full>"         # 255
+    assert name(1, 1, 4096, 64, False, osa.ATTN_F32) == "fused_fwd32_split<full>"
+    assert name(8, 64, 4096, 64, True, osa.ATTN_F32) == "fused_fwd32<causal>"
+    assert name(4, 12, 8192, 128, True, osa.ATTN_BF16) == "fused_hd16<bf16, causal, 128>"
+    assert name(4, 12, 8192, 32, False, osa.ATTN_F16) == "fused_hd16<f16, full, 32>"
+    lib = binding.load()
+    assert lib.attn_fused_kernel(0, 1, 8, 64, 1, 1) == -1
+    assert lib.attn_fused_kernel(1, 1, 8, 64, 1, 7) == -1
+    assert lib.attn_fused_kernel(1, 1, 8, 48, 1, 1) == -2
+    assert lib.attn_fused_kernel(1, 1, 8, 128, 1, 0) == -2
 
 
 def test_metric_workload_floor():
@@ -313,7 +338,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 83
+    assert n == 87
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None

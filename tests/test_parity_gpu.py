@@ -141,6 +141,62 @@ def test_ragged_16bit(gpu_lib, dtype, causal, T):
                f"ragged_{dtype}_c{int(causal)}_t{T}")
 
 
+# --- the eight-wave 16-bit kernel at small shapes ---------------------------------
+# Many heads bring short sequences to its grid threshold (B*H*ceil(T/256) >=
+# 256), so ragged lengths, waves whose rows all lie past T in the last query
+# tile, and each wave's masked tail are checked element by element.
+
+W8_SHAPES = [(4, 64, 1), (4, 64, 77), (2, 64, 300), (1, 128, 513), (1, 32, 2100)]
+
+
+def assert_eight_wave(gpu_lib, B, H, T, causal, dtype):
+    code = {"bf16": gpu_lib.ATTN_BF16, "f16": gpu_lib.ATTN_F16}[dtype]
+    name = gpu_lib.attn_kernel_name(gpu_lib.attn_fused_kernel(B, H, T, D, causal, code))
+    assert name.startswith("fused_fwd16w8"), name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", W8_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_eight_wave_kernel(gpu_lib, dtype, causal, shape):
+    B, H, T = shape
+    assert_eight_wave(gpu_lib, B, H, T, causal, dtype)
+    q, k, v = make_qkv(B, H, T, D, dtype, 2100 + T + 7 * H)
+    check_full(gpu_lib, q, k, v, causal, 0.125, dtype,
+               f"w8_{dtype}_c{int(causal)}_{B}x{H}x{T}")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
+def test_eight_wave_scale_sign_and_zero(gpu_lib, scale):
+    assert_eight_wave(gpu_lib, 2, 64, 300, True, "bf16")
+    q, k, v = make_qkv(2, 64, 300, D, "bf16", 2200)
+    check_full(gpu_lib, q, k, v, True, scale, "bf16", f"w8_scale_{scale}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_eight_wave_rising_scores(gpu_lib, causal):
+    """The rising-keys stress input (keys x1 -> x6 along the sequence) on the
+    eight-wave kernel: the lazy reference must hand over to the full update
+    inside the unmasked loop and in the masked tail."""
+    B, H, T = 1, 16, 4096
+    assert_eight_wave(gpu_lib, B, H, T, causal, "bf16")
+    q, k, v = make_qkv(B, H, T, D, "f32", 2300)
+    ramp = torch.linspace(1.0, 6.0, T).reshape(1, 1, T, 1)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k * ramp, v))
+    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"w8_rising_c{int(causal)}")
+
+
+def test_eight_wave_lse_optional(gpu_lib):
+    assert_eight_wave(gpu_lib, 2, 64, 300, True, "bf16")
+    q, k, v = make_qkv(2, 64, 300, D, "bf16", 2400)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o1 = torch.empty_like(qd)
+    gpu_lib.attn_fwd_stream(qd, kd, vd, o1, None, True, 0.125)
+    o2, _ = gpu_lib.attention(qd, kd, vd, True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 @pytest.mark.parametrize("T", [77, 300])
 def test_bf16_within_twice_torch_cpu_error(gpu_lib, T):
     """The rule of "Flash attention in PyTorch, then in Triton" (section "A
