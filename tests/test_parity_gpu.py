@@ -186,6 +186,41 @@ def test_eight_wave_rising_scores(gpu_lib, causal):
     check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"w8_rising_c{int(causal)}")
 
 
+def test_eight_wave_single_token_returns_v_exactly(gpu_lib):
+    """T = 1 on the eight-wave kernel: the lone weight is exp2(0) = 1, so O is
+    V bit for bit once rounded to bf16."""
+    assert_eight_wave(gpu_lib, 4, 64, 1, True, "bf16")
+    q, k, v = make_qkv(4, 64, 1, D, "bf16", 2500)
+    o, _ = fused(gpu_lib, q, k, v, True, 0.125)
+    assert torch.equal(o.to(v.dtype), v)
+
+
+def test_eight_wave_zero_query_prefix_mean(gpu_lib):
+    """Q = 0 on the eight-wave kernel: every visible key weighs the same, so
+    O_i is the mean of V_0..V_i and lse_i = ln(i + 1) (closed form)."""
+    B, H, T = 2, 64, 300
+    assert_eight_wave(gpu_lib, B, H, T, True, "bf16")
+    _, k, v = make_qkv(B, H, T, D, "bf16", 2600)
+    q = torch.zeros_like(k)
+    o, lse = fused(gpu_lib, q, k, v, True, 0.125)
+    counts = np.arange(1, T + 1, dtype=np.float64)
+    mean = np.cumsum(v.double().numpy(), axis=2) / counts[None, None, :, None]
+    assert_close("w8 Q=0 O", o.numpy(), mean, tol("bf16", T))
+    assert_close("w8 Q=0 lse", lse.numpy(), np.broadcast_to(np.log(counts), lse.shape),
+                 tol("bf16", T))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_eight_wave_late_spike(gpu_lib, causal):
+    """The late-spike stress input (one key near the end amplified) on every
+    head of a grid large enough for the eight-wave kernel."""
+    T, H = 1000, 64
+    assert_eight_wave(gpu_lib, 1, H, T, causal, "bf16")
+    q, k, v = late_spike_qkv(T, D, "bf16")
+    q, k, v = (x.expand(1, H, T, D).contiguous() for x in (q, k, v))
+    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"w8_late_spike_c{int(causal)}")
+
+
 def test_eight_wave_lse_optional(gpu_lib):
     assert_eight_wave(gpu_lib, 2, 64, 300, True, "bf16")
     q, k, v = make_qkv(2, 64, 300, D, "bf16", 2400)
