@@ -93,6 +93,9 @@ typedef enum { ATTN_PATH_FUSED = 0, ATTN_PATH_NAIVE = 1 } attn_path;
  * bytes per (batch, head) slice (one K or V slice is addressed as a single
  * buffer).
  * Extra device memory: none (the caller's lse is the only O(T) side output).
+ * The kernel launched depends on dtype, D and the grid size
+ * (attn_fused_kernel names it); every kernel computes the same result to
+ * rounding.
  */
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o,
                     float* lse, int B, int H, int T, int D, int causal,

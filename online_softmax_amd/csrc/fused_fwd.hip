@@ -496,9 +496,9 @@ __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
     // reference max starts finite (-FLT_MAX): no inf - inf, and scale 0 works
     RowState st = {-FLT_MAX, -FLT_MAX * c, 0.f};
 
-    // One tile. The fragment reads go in groups of four (16 registers),
-    // fenced from the scheduler, so a wave stays within 128 VGPRs: the LDS
-    // latency a wave then waits out is covered by the SIMD's other waves.
+    // One tile. The fragment reads are written in groups of four (16
+    // registers) and the compiler orders them within the 128-VGPR budget;
+    // the LDS latency a wave waits out is covered by the SIMD's other waves.
     typedef __attribute__((address_space(3))) char lds_char;
     typedef __attribute__((address_space(3))) v4u32 lds_v4u32;
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
