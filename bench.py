@@ -676,6 +676,50 @@ def forward_case(osa, torch, oracle, B, H, T, dtype, seed, steps, warmup,
     return out
 
 
+def context_leg(osa, torch, w, qd, kd, vd, steps=20):
+    """Two other programs on the same chip, for context (neither is part of
+    the path): torch's own fused attention (scaled_dot_product_attention,
+    flash backend only, on the metric's inputs: the comparison the page
+    "Flash attention in PyTorch, then in Triton" draws in section "A kernel
+    in Triton"), and the vendor library's dense bf16 matrix product
+    (torch.matmul, 8192^3, seeded N(0,1) operands), the matrix-core rate a
+    plain GEMM reaches here. Only the flash backend is allowed: if it cannot
+    run the call, the leg records why instead of falling back to the math
+    path."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    stream = torch.cuda.current_stream()
+    out = {}
+    flops = osa.attn_flops(w.B, w.H, w.T, w.D, w.causal)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            run = lambda: torch.nn.functional.scaled_dot_product_attention(
+                qd, kd, vd, is_causal=w.causal, scale=w.scale)
+            ref = run()
+            r = timed_calls(torch, run, stream, steps)
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=qd.device)
+        osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale, stream)
+        torch.cuda.synchronize()
+        out["torch_sdpa"] = {"ms": r["mean"], "tflops": flops / (r["mean"] * 1e-3) / 1e12,
+                             "max_abs_diff_to_ours": float((ref.float() - o.float()).abs().max())}
+        del ref, o, lse
+    except RuntimeError as e:
+        out["torch_sdpa"] = {"error": str(e)[:200]}
+    n = 8192
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(qd.device)
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to(qd.device)
+    r = timed_calls(torch, lambda: torch.matmul(a, b), stream, steps)
+    out["gemm_bf16_8192"] = {"ms": r["mean"], "tflops": 2 * n**3 / (r["mean"] * 1e-3) / 1e12}
+    del a, b
+    torch.cuda.synchronize()
+    s = out["torch_sdpa"]
+    log("context: torch SDPA (flash) " + (f"{s['ms']:.4f} ms, {s['tflops']:.1f} TFLOP/s"
+                                           if "ms" in s else s["error"])
+        + f"; bf16 GEMM 8192^3 {out['gemm_bf16_8192']['tflops']:.1f} TFLOP/s")
+    return out
+
+
 def memory_contrast(osa, torch, w):
     """Device memory held by each forward path at the metric's B, H and T,
     measured by the caching allocator's peak around one call (the library
@@ -757,6 +801,8 @@ def main():
                     help="skip the head dimension 32 / 128 legs")
     ap.add_argument("--no-recurrence", action="store_true",
                     help="skip the gated linear recurrence leg")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip timing torch's own fused attention and a bf16 GEMM")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB "
                          "(reference kernel for PMC byte counters)")
@@ -826,6 +872,10 @@ def main():
         f"{t['host_ms']:.3f} ms host-side; {achieved:.1f} TFLOP/s = "
         f"{100 * achieved / peak:.1f}% of {peak} TFLOP/s")
     del o, lse
+
+    ctx = None
+    if not a.no_context and w.dtype != "f32":
+        ctx = context_leg(osa, torch, w, qd, kd, vd)
 
     sweep = long_ctx = None
     if not a.no_sweep and w.name == METRIC_WORKLOAD:
@@ -900,7 +950,8 @@ def main():
         "long_context": long_ctx, "memory": mem, "backward": bwd,
         "backward_atomic": bwd_atomic, "cpu_single_core": single, "decode": dec,
         "decode_d128": dec128, "head_dims": hds, "gated_recurrence": recur,
-        "contrast_fp32_single_head": extra, "kernel_source_sha256": kernel_source_hash()}
+        "contrast_fp32_single_head": extra, "context": ctx,
+        "kernel_source_sha256": kernel_source_hash()}
     log("bench detail: " + json.dumps(detail))
     if a.detail:
         with open(a.detail, "w") as f:
@@ -941,6 +992,9 @@ def main():
                  "decode_d128": leg(dec128),
                  "d32": leg((hds or {}).get("32")), "d128": leg((hds or {}).get("128")),
                  "recurrence": leg((recur or {}).get("throughput"))},
+        "context_tflops": None if ctx is None else
+            {"torch_sdpa_flash": ctx["torch_sdpa"].get("tflops"),
+             "gemm_bf16_8192": ctx["gemm_bf16_8192"]["tflops"]},
     }
     sys.stderr.flush()
     print(json.dumps(compact(line), separators=(",", ":")), flush=True)
