@@ -347,10 +347,12 @@ int attn_kernel_attributes(int kernel, attn_kernel_attr* out);
  * queries per workgroup and keys per LDS tile for `dtype`. A float32 call
  * whose grid would have fewer than 256 such workgroups (B*H*ceil(T/128))
  * runs a kernel that splits the keys among the waves of a workgroup of 32
- * query rows instead; a 16-bit call with D = 64 whose grid of 256-row
- * workgroups has at least 256 of them (B*H*ceil(T/256) >= 256) runs the
- * eight-wave kernel on 256 query rows per workgroup. attn_traffic_bytes
- * counts the tiles of the kernel that runs. */
+ * query rows instead. A 16-bit call with D = 64 runs the eight-wave kernel
+ * on 256 query rows per workgroup when full with B*H*ceil(T/256) >= 256,
+ * or causal with B*H*(ceil(T/256) + 1) >= 600; other causal calls, and
+ * full calls with B*H*ceil(T/128) <= 256, run its key-split form (128
+ * query rows per workgroup, the key tiles shared out between two groups of
+ * waves). attn_traffic_bytes counts the tiles of the kernel that runs. */
 int attn_fused_tile(int dtype, int* block_m, int* block_n);
 
 /* The kernel attn_fwd / attn_fwd_stream launch for these arguments, as an

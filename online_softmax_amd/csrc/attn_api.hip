@@ -387,8 +387,10 @@ int attn_fused_kernel(int B, int H, int T, int D, int causal, int dtype) {
                         attn::kDecodeKernels;
         return hd0 + (D == 128 ? 4 : 0) + f16 + full;
     }
-    if (attn::fwd16_eight_waves(bh, T))
+    if (attn::fwd16_eight_waves(bh, T, causal != 0))
         return attn_kernel_count() - attn::kFwdW8Kernels + f16 + full;
+    if (attn::fwd16_key_split(bh, T, causal != 0))
+        return attn_kernel_count() - attn::kFwdW8Kernels + 4 + f16 + full;
     return f16 + full;
 }
 
@@ -418,7 +420,8 @@ int attn_traffic_bytes(int path, int B, int H, int T, int D, int dtype,
         // fp32 on a small grid runs the key-split kernel on 32-row tiles;
         // 16-bit D = 64 on a large one the eight-wave kernel on 256-row tiles
         if (dtype == ATTN_F32 && attn::fwd32_split((long long)bh, T)) bm = attn::kSplitRows;
-        if (dtype != ATTN_F32 && D == attn::kHeadDim && attn::fwd16_eight_waves((long long)bh, T))
+        if (dtype != ATTN_F32 && D == attn::kHeadDim &&
+            attn::fwd16_eight_waves((long long)bh, T, causal != 0))
             bm = attn::kBlockM8;
         const int nq = (T + bm - 1) / bm;
         uint64_t kv_rows = 0;
@@ -513,7 +516,9 @@ const char* attn_kernel_name(int kernel) {
         "decode_merged16<bf16, causal, 128>", "decode_merged16<bf16, full, 128>",
         "decode_merged16<f16, causal, 128>", "decode_merged16<f16, full, 128>",
         "fused_fwd16w8<bf16, causal>", "fused_fwd16w8<bf16, full>",
-        "fused_fwd16w8<f16, causal>",  "fused_fwd16w8<f16, full>"};
+        "fused_fwd16w8<f16, causal>",  "fused_fwd16w8<f16, full>",
+        "fused_fwd16w8s<bf16, causal>", "fused_fwd16w8s<bf16, full>",
+        "fused_fwd16w8s<f16, causal>",  "fused_fwd16w8s<f16, full>"};
     if (kernel < 0 || kernel >= attn_kernel_count()) return nullptr;
     return names[kernel];
 }

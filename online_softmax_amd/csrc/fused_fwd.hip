@@ -419,13 +419,25 @@ __global__ __launch_bounds__(kThreads, 2) void fused_fwd16(
 // tile t + 3 issued after the barrier of iteration t into the stage tile
 // t - 1 used. Each wave computes only its own tiles (w8_seen) and masks only
 // its own diagonal and the ragged tile (w8_main); it joins every barrier.
+//
+// SPLIT = kSplit8 is the key-split form for small grids: waves w and
+// w + 4 own the same 32 rows (128 per workgroup), and in iteration i the
+// two groups compute tiles 2i and 2i + 1, both loaded by all eight waves
+// (the pair for iteration i + 1 is issued after iteration i's barrier into
+// the stages of the pair before). At the end the second group hands its
+// O, reference and denominator to the first through LDS, which merges
+// them by the same rescale as any reference move: the reference becomes
+// the larger of the two and each side is scaled by exp2(its - new).
 // ---------------------------------------------------------------------------
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, int SPLIT>
 __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
+    static_assert(SPLIT == 1 || SPLIT == kSplit8, "one or two key groups");
     constexpr int BN = kBlockN16;
+    constexpr int RW = kWaves8 / SPLIT;  // waves per key group, one per 32 rows
+    constexpr int BM = 32 * RW;          // query rows per workgroup
     __shared__ __attribute__((aligned(1024))) char kring[kRing8][kTileBytes16];
     __shared__ __attribute__((aligned(1024))) char vring[kRing8][kTileBytes16];
 
@@ -435,14 +447,16 @@ __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
     const int ql = lane & 31;
     const int hh = lane >> 5;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // uniform copy
+    const int rw = SPLIT == 1 ? wave_u : wave_u % RW;  // which 32 rows
+    const int grp = SPLIT == 1 ? 0 : wave_u / RW;      // key group: tiles t % SPLIT == grp
 
     int bh, qt;
     tile_of8(blockIdx.x, gridDim.x, nq, CAUSAL, &bh, &qt);
     const int64_t base = (int64_t)bh * T * kHeadDim;
-    const int wq0 = qt * kBlockM8 + 32 * wave_u;  // first query row of this wave
-    const int my_q = wq0 + ql;                    // this lane's query row
-    const int n_tiles = key_tiles(qt, T, BN, CAUSAL, kBlockM8);
-    const int n_seen = w8_seen(qt, wave_u, T, CAUSAL);
+    const int wq0 = qt * BM + 32 * rw;  // first query row of this wave
+    const int my_q = wq0 + ql;          // this lane's query row
+    const int n_tiles = key_tiles(qt, T, BN, CAUSAL, BM);
+    const int n_seen = w8_seen(qt, rw, T, CAUSAL, BM);
 
     // Q rows first: their loads are older than every ring load, so the
     // first tile's wait covers them too
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
         load_tile(krs, kring[t % kRing8], kvoff, t);
         load_tile(vrs, vring[t % kRing8], vvoff, t);
     };
-    for (int t = 0; t < kAhead8 && t < n_tiles; ++t) issue(t);
+    for (int t = 0; t < (SPLIT == 1 ? kAhead8 : SPLIT) && t < n_tiles; ++t) issue(t);
 
     // Fragment addresses from one lane base per tile each: the swizzles only
     // permute 16-byte chunks within a row and the stages are 8 KiB aligned,
@@ -543,17 +557,27 @@ __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
         }
     };
     auto sync_issue = [&](int t) {
-        // this wave's loads of tile t (and the Q rows) have landed; those of
-        // the (up to two) later tiles already issued may still be in flight
-        const int ahead = min(kAhead8 - 1, n_tiles - 1 - t);
-        if (ahead >= 2)
-            wait_vmcnt<4>();
-        else if (ahead == 1)
-            wait_vmcnt<2>();
-        else
+        if (SPLIT == 1) {
+            // this wave's loads of tile t (and the Q rows) have landed; those
+            // of the (up to two) later tiles already issued may still be in
+            // flight
+            const int ahead = min(kAhead8 - 1, n_tiles - 1 - t);
+            if (ahead >= 2)
+                wait_vmcnt<4>();
+            else if (ahead == 1)
+                wait_vmcnt<2>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();  // everyone's share landed; tile t - 1's stages are free
+            if (t + kAhead8 < n_tiles) issue(t + kAhead8);
+        } else {
+            // t is the iteration: its pair of tiles (and the Q rows) landed
             wait_vmcnt<0>();
-        __syncthreads();  // everyone's share landed; tile t - 1's stages are free
-        if (t + kAhead8 < n_tiles) issue(t + kAhead8);
+            __syncthreads();  // the previous pair's stages are free
+#pragma unroll
+            for (int j = 0; j < SPLIT; ++j)
+                if (SPLIT * (t + 1) + j < n_tiles) issue(SPLIT * (t + 1) + j);
+        }
     };
     // Tiles every wave computes unmasked (those before the first wave's
     // first masked one), then the last few (at most four), where each wave
@@ -561,22 +585,51 @@ __global__ __launch_bounds__(kThreads8, 4) void fused_fwd16w8(
     // mask it masks nothing and takes the same decisions, so the results
     // are the same bits, and one step form keeps the tail within the
     // register budget.
-    const int n_all_main = w8_main(qt, 0, T, CAUSAL);
-    int t = 0;
-    for (; t < n_all_main; ++t) {
-        sync_issue(t);
+    // (key split: iteration i, tile SPLIT * i + grp; the unmasked loop runs
+    // while both tiles of the pair are unmasked for every wave)
+    const int n_all_main = w8_main(qt, 0, T, CAUSAL, BM);
+    const int n_iter = (n_tiles + SPLIT - 1) / SPLIT;
+    int i = 0;
+    for (; i < n_all_main / SPLIT; ++i) {
+        sync_issue(i);
+        const int t = SPLIT * i + grp;
         if (t < n_seen) step(t, std::integral_constant<bool, false>());  // rows < T
     }
-    for (; t < n_tiles; ++t) {
-        sync_issue(t);
+    for (; i < n_iter; ++i) {
+        sync_issue(i);
+        const int t = SPLIT * i + grp;
         if (t < n_seen) step(t, std::integral_constant<bool, true>());
+    }
+    if (SPLIT > 1) {
+        // group 1 hands O, mc and l (lane by lane: the partner lane holds the
+        // same row and dims) to group 0 through the rings, now free
+        __syncthreads();
+        float* xo = (float*)&kring[0][0];  // [RW][32][64]: 32 KiB
+        float* xs = (float*)&vring[0][0];  // [RW][2][64]
+        if (grp == 1) {
+#pragma unroll
+            for (int r = 0; r < 32; ++r) xo[(rw * 32 + r) * 64 + lane] = oacc[r >> 4][r & 15];
+            xs[(rw * 2) * 64 + lane] = st.mc;
+            xs[(rw * 2 + 1) * 64 + lane] = st.l;
+        }
+        __syncthreads();
+        if (grp != 0) return;
+        const float mc1 = xs[(rw * 2) * 64 + lane], l1 = xs[(rw * 2 + 1) * 64 + lane];
+        const float mcn = fmaxf(st.mc, mc1);
+        const float a0 = fast_exp2(st.mc - mcn), a1 = fast_exp2(mc1 - mcn);
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+            oacc[r >> 4][r & 15] = oacc[r >> 4][r & 15] * a0 + xo[(rw * 32 + r) * 64 + lane] * a1;
+        st.l = st.l * a0 + l1 * a1;
+        st.mc = mcn;
     }
 
     // the output row from an opaque copy of the thread index, so its address
     // is not computed before the loop and carried through it
     int tid_late = tid;
     asm("" : "+v"(tid_late));
-    const int row = qt * kBlockM8 + 32 * (tid_late >> 6) + (tid_late & 31);
+    const int row =
+        qt * BM + 32 * (SPLIT == 1 ? tid_late >> 6 : (tid_late >> 6) % RW) + (tid_late & 31);
     const float lt = halves_sum(st.l);
     const float inv = 1.0f / lt;
     if (row < T) {
@@ -963,14 +1016,16 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, void* o,
                                (const float*)q, (const float*)k, (const float*)v, (float*)o,
                                lse, T, nq, c, sign);
         }
-    } else if (fwd16_eight_waves(BH, T)) {
-        const int nq = (T + kBlockM8 - 1) / kBlockM8;
+    } else if (fwd16_eight_waves(BH, T, causal != 0) || fwd16_key_split(BH, T, causal != 0)) {
+        const bool split = !fwd16_eight_waves(BH, T, causal != 0);
+        const int bm = split ? kBlockM8s : kBlockM8;
+        const int nq = (T + bm - 1) / bm;
         const dim3 grid((unsigned)(nq * BH));
         const dim3 block(kThreads8);
         const uint32_t sign = negate_q ? 0x80008000u : 0u;
-        auto fn = dt == ATTN_DT_BF16
-                      ? (causal ? fused_fwd16w8<ATTN_DT_BF16, true> : fused_fwd16w8<ATTN_DT_BF16, false>)
-                      : (causal ? fused_fwd16w8<ATTN_DT_F16, true> : fused_fwd16w8<ATTN_DT_F16, false>);
+        const int index = (split ? 4 : 0) + (dt == ATTN_DT_F16 ? 2 : 0) + (causal ? 0 : 1);
+        auto fn = (void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*,
+                            int, int, float, uint32_t))fused_w8_kernel_ptr(index);
         hipLaunchKernelGGL(fn, grid, block, 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                            (const uint16_t*)v, (uint16_t*)o, lse, T, nq, c, sign);
     } else {
@@ -1009,12 +1064,18 @@ const void* fused_kernel_ptr(int index) {
     }
 }
 
+// Table order: the eight-wave kernel, then its key-split form; bf16 then
+// f16; causal then not.
 const void* fused_w8_kernel_ptr(int index) {
     switch (index) {
-        case 0: return (const void*)fused_fwd16w8<ATTN_DT_BF16, true>;
-        case 1: return (const void*)fused_fwd16w8<ATTN_DT_BF16, false>;
-        case 2: return (const void*)fused_fwd16w8<ATTN_DT_F16, true>;
-        case 3: return (const void*)fused_fwd16w8<ATTN_DT_F16, false>;
+        case 0: return (const void*)fused_fwd16w8<ATTN_DT_BF16, true, 1>;
+        case 1: return (const void*)fused_fwd16w8<ATTN_DT_BF16, false, 1>;
+        case 2: return (const void*)fused_fwd16w8<ATTN_DT_F16, true, 1>;
+        case 3: return (const void*)fused_fwd16w8<ATTN_DT_F16, false, 1>;
+        case 4: return (const void*)fused_fwd16w8<ATTN_DT_BF16, true, kSplit8>;
+        case 5: return (const void*)fused_fwd16w8<ATTN_DT_BF16, false, kSplit8>;
+        case 6: return (const void*)fused_fwd16w8<ATTN_DT_F16, true, kSplit8>;
+        case 7: return (const void*)fused_fwd16w8<ATTN_DT_F16, false, kSplit8>;
         default: return nullptr;
     }
 }

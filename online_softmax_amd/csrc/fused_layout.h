@@ -204,8 +204,8 @@ constexpr int kAhead8 = kRing8 - 1;
 // causal, <= the wave's first row). The wave's tiles between the two (at
 // most its diagonal tile and the ragged last tile) take the masked step.
 // A wave whose rows all lie past T computes none.
-ATTN_HD int w8_seen(int qt, int w, int T, bool causal) {
-    const int wq0 = qt * kBlockM8 + 32 * w;
+ATTN_HD int w8_seen(int qt, int w, int T, bool causal, int bm = kBlockM8) {
+    const int wq0 = qt * bm + 32 * w;
     if (wq0 >= T) return 0;
     const int all = (T + kBlockN16 - 1) / kBlockN16;
     if (!causal) return all;
@@ -213,15 +213,15 @@ ATTN_HD int w8_seen(int qt, int w, int T, bool causal) {
     const int n = last / kBlockN16 + 1;
     return n < all ? n : all;
 }
-ATTN_HD int w8_main(int qt, int w, int T, bool causal) {
-    const int wq0 = qt * kBlockM8 + 32 * w;
+ATTN_HD int w8_main(int qt, int w, int T, bool causal, int bm = kBlockM8) {
+    const int wq0 = qt * bm + 32 * w;
     if (wq0 >= T) return 0;
     int n = T / kBlockN16;
     if (causal) {
         const int c = (wq0 + 1) / kBlockN16;
         if (c < n) n = c;
     }
-    const int seen = w8_seen(qt, w, T, causal);
+    const int seen = w8_seen(qt, w, T, causal, bm);
     return n < seen ? n : seen;
 }
 // Workgroup -> (slice, 256-row query tile) of the eight-wave kernel. As in
@@ -242,11 +242,34 @@ ATTN_HD void tile_of8(int block, int total, int nq, bool causal, int* bh, int* q
     const int t = i / spx;
     *qt = causal ? nq - 1 - t : t;
 }
-// The eight-wave kernel runs when its grid has at least one workgroup per
-// CU; shorter calls keep the 128-row kernel, whose grid is twice as large.
+// Which 16-bit D = 64 forward a call runs.
+//  - The eight-wave kernel (256-row workgroups, K and V tiles shared by the
+//    most rows) on full calls whose grid has at least one workgroup per CU,
+//    and on causal calls whose heaviest query tile (4 nq key tiles, nq =
+//    ceil(T / 256)) is at most 7/4 of the work per workgroup slot (two per
+//    CU, 512 slots): 4 nq <= 7/4 * BH * 2 nq (nq + 1) / 512, that is
+//    BH (nq + 1) >= 585. Below that the heaviest tiles' key loops set the
+//    call's time (measured: the eight-wave kernel ahead by 5% at BH (nq + 1)
+//    = 640 and 816, behind by 2-28% from 544 down).
+//  - Otherwise its key-split form: kSplit8 groups of waves share the query
+//    rows (kBlockM8s = 128 per workgroup, twice the workgroups), group g
+//    computes the key tiles t with t % kSplit8 == g, and the groups'
+//    partial results merge through LDS at the end, so the heaviest tile
+//    runs half as many tiles in turn. Every causal call that does not take
+//    the eight-wave kernel takes this one; full calls take it while its
+//    grid has at most one workgroup per CU (kW8MinGrid).
+//  - Otherwise (full calls between the two) the 128-row kernel.
 constexpr int kW8MinGrid = 256;
-ATTN_HD bool fwd16_eight_waves(long long BH, int T) {
-    return (long long)((T + kBlockM8 - 1) / kBlockM8) * BH >= kW8MinGrid;
+constexpr int kW8CausalWork = 600;
+constexpr int kSplit8 = 2;
+constexpr int kBlockM8s = kBlockM8 / kSplit8;
+ATTN_HD bool fwd16_eight_waves(long long BH, int T, bool causal) {
+    const long long nq = (T + kBlockM8 - 1) / kBlockM8;
+    return causal ? BH * (nq + 1) >= kW8CausalWork : nq * BH >= kW8MinGrid;
+}
+ATTN_HD bool fwd16_key_split(long long BH, int T, bool causal) {
+    if (fwd16_eight_waves(BH, T, causal)) return false;
+    return causal || (long long)((T + kBlockM8s - 1) / kBlockM8s) * BH <= kW8MinGrid;
 }
 
 // ---- other head dimensions (16-bit forward, D = 32 or 128) -----------------

@@ -83,7 +83,7 @@ constexpr int kRecurrenceKernels = 16;
 constexpr int kBwdAtomicKernels = 8;
 constexpr int kDecodeHdKernels = 12;  // decode at D = 32 and 128 (decode_kernel_ptr 6 .. 17)
 constexpr int kDecodeMergedKernels = 12;  // decode without allocation, D = 64, 32, 128
-constexpr int kFwdW8Kernels = 4;          // 8-wave 16-bit forward, D = 64
+constexpr int kFwdW8Kernels = 8;          // 8-wave 16-bit forward and its key split, D = 64
 const void* fused_kernel_ptr(int index);
 const void* naive_kernel_ptr(int index);
 const void* bwd_kernel_ptr(int index);

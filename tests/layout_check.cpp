@@ -1063,6 +1063,100 @@ static void check_w8(int BH, int T, bool causal) {
     }
 }
 
+// The key-split form of the eight-wave kernel: workgroup -> (slice, 128-row
+// query tile) is a bijection; waves w and w + 4 own the same 32 rows, and in
+// iteration i group g computes tile 2i + g when one of those rows sees a key
+// in it. Every visible tile is computed by exactly one group, nothing else
+// is, the unmasked loop's tiles need no mask, every computed tile was
+// issued (the pair of iteration i in the prologue or after iteration
+// i - 1's barrier) into a stage no other tile of iterations i - 1 .. i holds,
+// and the merge buffers fit in the rings.
+static void check_w8_split(int BH, int T, bool causal) {
+    constexpr int BM = kBlockM8s, RW = kWaves8 / kSplit8;
+    static_assert(kSplit8 == 2 && BM == 32 * RW, "two key groups of four waves");
+    static_assert(RW * 32 * 64 * 4 <= kRing8 * kTileBytes16, "O hand-over fits the K ring");
+    static_assert(RW * 2 * 64 * 4 <= kRing8 * kTileBytes16, "mc, l hand-over fits the V ring");
+    const int nq = (T + BM - 1) / BM;
+    const int total = nq * BH;
+    std::vector<int> hit(total, 0);
+    for (int b = 0; b < total; ++b) {
+        int bh, qt;
+        tile_of8(b, total, nq, causal, &bh, &qt);
+        CHECK(bh >= 0 && bh < BH && qt >= 0 && qt < nq, "w8s tile_of8(%d)", b);
+        if (bh >= 0 && bh < BH && qt >= 0 && qt < nq) hit[bh * nq + qt]++;
+    }
+    for (int i = 0; i < total; ++i) CHECK(hit[i] == 1, "w8s tile %d hit %d times", i, hit[i]);
+    for (int qt = 0; qt < nq; ++qt) {
+        const int n_tiles = key_tiles(qt, T, kBlockN16, causal, BM);
+        const int n_all_main = w8_main(qt, 0, T, causal, BM);
+        const int n_iter = (n_tiles + kSplit8 - 1) / kSplit8;
+        CHECK(n_tiles >= 1 && n_all_main >= 0 && n_all_main <= n_tiles, "w8s T %d qt %d", T, qt);
+        // issue iteration of each tile: the prologue (-1) issues the first
+        // pair, iteration i the pair of iteration i + 1
+        std::vector<int> issued(n_tiles, -2);
+        for (int t = 0; t < kSplit8 && t < n_tiles; ++t) issued[t] = -1;
+        for (int i = 0; i < n_iter; ++i)
+            for (int j = 0; j < kSplit8; ++j) {
+                const int t = kSplit8 * (i + 1) + j;
+                if (t < n_tiles) issued[t] = i;
+            }
+        for (int t = 0; t < n_tiles; ++t) {
+            CHECK(issued[t] == t / kSplit8 - 1, "w8s tile %d issued at %d", t, issued[t]);
+            // no tile of iterations t/2 - 1 .. t/2 shares its stage
+            for (int u = std::max(0, (t / kSplit8 - 1) * kSplit8); u < t; ++u)
+                CHECK(u % kRing8 != t % kRing8, "w8s stage of tile %d held by tile %d", t, u);
+        }
+        for (int rw = 0; rw < RW; ++rw) {
+            const int wq0 = qt * BM + 32 * rw;
+            const int rlast = std::min(wq0 + 31, T - 1);
+            const int seen = w8_seen(qt, rw, T, causal, BM);
+            std::vector<int> done(n_tiles, 0);
+            for (int g = 0; g < kSplit8; ++g)
+                for (int i = 0; i < n_iter; ++i) {
+                    const int t = kSplit8 * i + g;
+                    if (t >= seen) continue;
+                    CHECK(t < n_tiles, "w8s T %d qt %d rw %d: tile %d not loaded", T, qt, rw, t);
+                    if (t >= n_tiles) continue;
+                    done[t]++;
+                    bool needs_mask = false;
+                    for (int r = wq0; r <= rlast; ++r)
+                        for (int key = t * kBlockN16; key < (t + 1) * kBlockN16; ++key)
+                            needs_mask = needs_mask || !(key < T && (!causal || key <= r));
+                    if (i < n_all_main / kSplit8)
+                        CHECK(!needs_mask, "w8s T %d qt %d rw %d: unmasked tile %d needs a mask",
+                              T, qt, rw, t);
+                }
+            for (int t = 0; t < n_tiles; ++t) {
+                bool vis = false;
+                for (int r = wq0; r <= rlast; ++r)
+                    for (int key = t * kBlockN16; key < (t + 1) * kBlockN16; ++key)
+                        vis = vis || (key < T && (!causal || key <= r));
+                CHECK(done[t] == (vis ? 1 : 0), "w8s T %d qt %d rw %d tile %d: computed %d times",
+                      T, qt, rw, t, done[t]);
+            }
+        }
+    }
+}
+
+// Which 16-bit D = 64 forward a call runs: the eight-wave kernel, its key
+// split or the 128-row kernel, exactly one; causal calls never take the
+// 128-row kernel, and the split's grid (128-row workgroups) is at most twice
+// the eight-wave one's.
+static void check_fwd16_dispatch() {
+    for (long long BH = 1; BH <= 600; BH += (BH < 64 ? 1 : 7))
+        for (int T : {1, 64, 200, 256, 257, 1000, 1024, 2048, 4096, 8192, 16384, 32768})
+            for (int causal = 0; causal < 2; ++causal) {
+                const bool w8 = fwd16_eight_waves(BH, T, causal);
+                const bool split = fwd16_key_split(BH, T, causal);
+                CHECK(!(w8 && split), "dispatch BH %lld T %d: both", BH, T);
+                if (causal) CHECK(w8 || split, "dispatch BH %lld T %d: causal 128-row", BH, T);
+                const long long nq8 = (T + kBlockM8 - 1) / kBlockM8;
+                if (!causal) CHECK(w8 == (nq8 * BH >= kW8MinGrid), "dispatch full BH %lld T %d", BH, T);
+            }
+    CHECK(fwd16_eight_waves(48, 8192, true), "the metric workload runs the eight-wave kernel");
+    CHECK(fwd16_key_split(48, 1024, true), "4 x 12 x 1024 causal runs the key split");
+}
+
 int main() {
     check_direct16();
     check_bwd_layout();
@@ -1138,6 +1232,11 @@ int main() {
         for (int BH : {1, 3, 8, 48})
             for (int causal = 0; causal < 2; ++causal) check_w8(BH, T, causal);
     for (int causal = 0; causal < 2; ++causal) check_w8(1, 8192, causal);
+    for (int T : {1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 513, 1000,
+                  1024, 2100, 4096})
+        for (int BH : {1, 3, 8, 16})
+            for (int causal = 0; causal < 2; ++causal) check_w8_split(BH, T, causal);
+    check_fwd16_dispatch();
     if (failures) {
         std::printf("%d failures\n", failures);
         return 1;

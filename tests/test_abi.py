@@ -282,17 +282,26 @@ def test_fused_traffic(dtype, causal, T):
 
 
 def test_fused_kernel_selection():
-    """attn_fused_kernel names the kernel attn_fwd launches: the eight-wave
-    16-bit kernel once its 256-row grid reaches 256 workgroups, the 128-row
-    one below, the fp32 key-split kernel on small fp32 grids, the head-dim
+    """attn_fused_kernel names the kernel attn_fwd launches. 16-bit, D = 64:
+    the eight-wave kernel on full calls once its 256-row grid reaches 256
+    workgroups and on causal calls once B*H*(ceil(T/256) + 1) >= 600; its
+    key-split form on the other causal calls and on full calls of at most
+    256 128-row workgroups; the 128-row kernel on the full calls between.
+    Then the fp32 key-split kernel on small fp32 grids and the head-dim
     kernels for D = 32 / 128; invalid arguments give attn_fwd's status."""
     name = lambda *a: osa.attn_kernel_name(osa.attn_fused_kernel(*a))
-    assert name(4, 12, 8192, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"
+    assert name(4, 12, 8192, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"   # 1584
     assert name(4, 12, 8192, 64, False, osa.ATTN_F16) == "fused_fwd16w8<f16, full>"
-    assert name(4, 12, 2048, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"  # 384
-    assert name(4, 12, 1024, 64, True, osa.ATTN_BF16) == "fused_fwd16<bf16, causal>"    # 192
-    assert name(1, 256, 1, 64, False, osa.ATTN_F16) == "fused_fwd16w8<f16, full>"       # 256
-    assert name(1, 255, 1, 64, False, osa.ATTN_F16) == "fused_fwd16<f16, full>"         # 255
+    assert name(4, 12, 4096, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"   # 816
+    assert name(8, 16, 1024, 64, True, osa.ATTN_BF16) == "fused_fwd16w8<bf16, causal>"   # 640
+    assert name(2, 16, 4096, 64, True, osa.ATTN_BF16) == "fused_fwd16w8s<bf16, causal>"  # 544
+    assert name(4, 12, 2048, 64, True, osa.ATTN_BF16) == "fused_fwd16w8s<bf16, causal>"  # 432
+    assert name(4, 12, 1024, 64, True, osa.ATTN_F16) == "fused_fwd16w8s<f16, causal>"    # 240
+    assert name(4, 12, 2048, 64, False, osa.ATTN_BF16) == "fused_fwd16w8<bf16, full>"    # 384
+    assert name(1, 256, 1, 64, False, osa.ATTN_F16) == "fused_fwd16w8<f16, full>"        # 256
+    assert name(4, 12, 1024, 64, False, osa.ATTN_BF16) == "fused_fwd16<bf16, full>"      # 384 rows/128
+    assert name(1, 255, 1, 64, False, osa.ATTN_F16) == "fused_fwd16w8s<f16, full>"       # 255 rows/128
+    assert name(1, 1, 300, 64, False, osa.ATTN_BF16) == "fused_fwd16w8s<bf16, full>"
     assert name(1, 1, 4096, 64, False, osa.ATTN_F32) == "fused_fwd32_split<full>"
     assert name(8, 64, 4096, 64, True, osa.ATTN_F32) == "fused_fwd32<causal>"
     assert name(4, 12, 8192, 128, True, osa.ATTN_BF16) == "fused_hd16<bf16, causal, 128>"
@@ -338,7 +347,7 @@ def test_traffic_other_head_dims(D):
 
 def test_kernel_table(lib):
     n = osa.attn_kernel_count()
-    assert n == 87
+    assert n == 91
     names = [osa.attn_kernel_name(i) for i in range(n)]
     assert all(names) and len(set(names)) == n
     assert osa.attn_kernel_name(n) is None

@@ -141,89 +141,124 @@ def test_ragged_16bit(gpu_lib, dtype, causal, T):
                f"ragged_{dtype}_c{int(causal)}_t{T}")
 
 
-# --- the eight-wave 16-bit kernel at small shapes ---------------------------------
-# Many heads bring short sequences to its grid threshold (B*H*ceil(T/256) >=
-# 256), so ragged lengths, waves whose rows all lie past T in the last query
-# tile, and each wave's masked tail are checked element by element.
+# --- the three 16-bit D = 64 kernels at small shapes ------------------------------
+# The eight-wave kernel (256-row workgroups), its key-split form (128 rows,
+# two groups of waves taking alternate key tiles and merging through LDS)
+# and the 128-row kernel, each on the shapes that select it: ragged
+# lengths, waves whose rows all lie past T in the last query tile, each
+# wave's masked tail, a key group with nothing to do (one key tile), checked
+# element by element. Many heads bring short sequences to the eight-wave
+# kernel's thresholds (full: B*H*ceil(T/256) >= 256; causal:
+# B*H*(ceil(T/256) + 1) >= 600).
 
-W8_SHAPES = [(4, 64, 1), (4, 64, 77), (2, 64, 300), (1, 128, 513), (1, 32, 2100)]
+KERNEL = {"w8": "fused_fwd16w8<", "w8s": "fused_fwd16w8s<", "r128": "fused_fwd16<"}
+
+# (kernel, (B, H, T), causal)
+KERNEL_CASES = (
+    [("w8", s, c) for s in [(8, 64, 1), (8, 64, 77), (4, 64, 300), (2, 128, 513), (1, 64, 2100)]
+     for c in (True, False)]
+    + [("w8s", s, True) for s in [(1, 1, 1), (4, 64, 1), (4, 64, 77), (2, 64, 300), (1, 128, 513),
+                                  (1, 32, 2100)]]
+    + [("w8s", s, False) for s in [(1, 1, 1), (1, 1, 300), (2, 3, 1000), (1, 8, 2100)]]
+    + [("r128", s, False) for s in [(1, 16, 2100), (4, 12, 1024)]])
 
 
-def assert_eight_wave(gpu_lib, B, H, T, causal, dtype):
+def assert_kernel(gpu_lib, kernel, B, H, T, causal, dtype):
     code = {"bf16": gpu_lib.ATTN_BF16, "f16": gpu_lib.ATTN_F16}[dtype]
     name = gpu_lib.attn_kernel_name(gpu_lib.attn_fused_kernel(B, H, T, D, causal, code))
-    assert name.startswith("fused_fwd16w8"), name
+    assert name.startswith(KERNEL[kernel]), (kernel, name)
+
+
+def case_id(c):
+    return f"{c[0]}_{'x'.join(map(str, c[1]))}_c{int(c[2])}"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("shape", W8_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_eight_wave_kernel(gpu_lib, dtype, causal, shape):
-    B, H, T = shape
-    assert_eight_wave(gpu_lib, B, H, T, causal, dtype)
+@pytest.mark.parametrize("case", KERNEL_CASES, ids=case_id)
+def test_kernel_small_shapes(gpu_lib, dtype, case):
+    kernel, (B, H, T), causal = case
+    assert_kernel(gpu_lib, kernel, B, H, T, causal, dtype)
     q, k, v = make_qkv(B, H, T, D, dtype, 2100 + T + 7 * H)
     check_full(gpu_lib, q, k, v, causal, 0.125, dtype,
-               f"w8_{dtype}_c{int(causal)}_{B}x{H}x{T}")
+               f"{kernel}_{dtype}_c{int(causal)}_{B}x{H}x{T}")
+
+
+# the eight-wave kernel and its key split, causal, at one shape each
+CAUSAL_PAIR = [("w8", (4, 64, 300)), ("w8s", (2, 64, 300))]
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
-def test_eight_wave_scale_sign_and_zero(gpu_lib, scale):
-    assert_eight_wave(gpu_lib, 2, 64, 300, True, "bf16")
-    q, k, v = make_qkv(2, 64, 300, D, "bf16", 2200)
-    check_full(gpu_lib, q, k, v, True, scale, "bf16", f"w8_scale_{scale}")
+@pytest.mark.parametrize("case", CAUSAL_PAIR, ids=lambda c: c[0])
+def test_eight_wave_scale_sign_and_zero(gpu_lib, case, scale):
+    kernel, (B, H, T) = case
+    assert_kernel(gpu_lib, kernel, B, H, T, True, "bf16")
+    q, k, v = make_qkv(B, H, T, D, "bf16", 2200)
+    check_full(gpu_lib, q, k, v, True, scale, "bf16", f"{kernel}_scale_{scale}")
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_eight_wave_rising_scores(gpu_lib, causal):
-    """The rising-keys stress input (keys x1 -> x6 along the sequence) on the
-    eight-wave kernel: the lazy reference must hand over to the full update
-    inside the unmasked loop and in the masked tail."""
-    B, H, T = 1, 16, 4096
-    assert_eight_wave(gpu_lib, B, H, T, causal, "bf16")
+@pytest.mark.parametrize("case", [("w8", (2, 40, 2048), True), ("w8", (2, 40, 2048), False),
+                                  ("w8s", (1, 16, 4096), True), ("w8s", (1, 8, 4096), False)],
+                         ids=case_id)
+def test_eight_wave_rising_scores(gpu_lib, case):
+    """The rising-keys stress input (keys x1 -> x6 along the sequence): the
+    lazy reference must hand over to the full update inside the unmasked
+    loop and in the masked tail, and (key split) the two groups' references
+    differ by the time they merge."""
+    kernel, (B, H, T), causal = case
+    assert_kernel(gpu_lib, kernel, B, H, T, causal, "bf16")
     q, k, v = make_qkv(B, H, T, D, "f32", 2300)
     ramp = torch.linspace(1.0, 6.0, T).reshape(1, 1, T, 1)
     q, k, v = (x.to(torch.bfloat16) for x in (q, k * ramp, v))
-    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"w8_rising_c{int(causal)}")
+    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"{kernel}_rising_c{int(causal)}")
 
 
-def test_eight_wave_single_token_returns_v_exactly(gpu_lib):
-    """T = 1 on the eight-wave kernel: the lone weight is exp2(0) = 1, so O is
-    V bit for bit once rounded to bf16."""
-    assert_eight_wave(gpu_lib, 4, 64, 1, True, "bf16")
-    q, k, v = make_qkv(4, 64, 1, D, "bf16", 2500)
-    o, _ = fused(gpu_lib, q, k, v, True, 0.125)
+@pytest.mark.parametrize("case", [("w8", (8, 64, 1), True), ("w8s", (4, 64, 1), True),
+                                  ("w8s", (1, 1, 1), False)], ids=case_id)
+def test_eight_wave_single_token_returns_v_exactly(gpu_lib, case):
+    """T = 1: the lone weight is exp2(0) = 1, so O is V bit for bit once
+    rounded to bf16 (in the key split the second group has no tile and
+    merges with weight 0)."""
+    kernel, (B, H, T), causal = case
+    assert_kernel(gpu_lib, kernel, B, H, T, causal, "bf16")
+    q, k, v = make_qkv(B, H, T, D, "bf16", 2500)
+    o, _ = fused(gpu_lib, q, k, v, causal, 0.125)
     assert torch.equal(o.to(v.dtype), v)
 
 
-def test_eight_wave_zero_query_prefix_mean(gpu_lib):
-    """Q = 0 on the eight-wave kernel: every visible key weighs the same, so
-    O_i is the mean of V_0..V_i and lse_i = ln(i + 1) (closed form)."""
-    B, H, T = 2, 64, 300
-    assert_eight_wave(gpu_lib, B, H, T, True, "bf16")
+@pytest.mark.parametrize("case", CAUSAL_PAIR, ids=lambda c: c[0])
+def test_eight_wave_zero_query_prefix_mean(gpu_lib, case):
+    """Q = 0: every visible key weighs the same, so O_i is the mean of
+    V_0..V_i and lse_i = ln(i + 1) (closed form)."""
+    kernel, (B, H, T) = case
+    assert_kernel(gpu_lib, kernel, B, H, T, True, "bf16")
     _, k, v = make_qkv(B, H, T, D, "bf16", 2600)
     q = torch.zeros_like(k)
     o, lse = fused(gpu_lib, q, k, v, True, 0.125)
     counts = np.arange(1, T + 1, dtype=np.float64)
     mean = np.cumsum(v.double().numpy(), axis=2) / counts[None, None, :, None]
-    assert_close("w8 Q=0 O", o.numpy(), mean, tol("bf16", T))
-    assert_close("w8 Q=0 lse", lse.numpy(), np.broadcast_to(np.log(counts), lse.shape),
+    assert_close(f"{kernel} Q=0 O", o.numpy(), mean, tol("bf16", T))
+    assert_close(f"{kernel} Q=0 lse", lse.numpy(), np.broadcast_to(np.log(counts), lse.shape),
                  tol("bf16", T))
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_eight_wave_late_spike(gpu_lib, causal):
+@pytest.mark.parametrize("case", [("w8", (1, 128, 1000), True), ("w8", (1, 64, 1000), False),
+                                  ("w8s", (1, 64, 1000), True), ("w8s", (1, 16, 1000), False)],
+                         ids=case_id)
+def test_eight_wave_late_spike(gpu_lib, case):
     """The late-spike stress input (one key near the end amplified) on every
-    head of a grid large enough for the eight-wave kernel."""
-    T, H = 1000, 64
-    assert_eight_wave(gpu_lib, 1, H, T, causal, "bf16")
+    head of the grid."""
+    kernel, (B, H, T), causal = case
+    assert_kernel(gpu_lib, kernel, B, H, T, causal, "bf16")
     q, k, v = late_spike_qkv(T, D, "bf16")
-    q, k, v = (x.expand(1, H, T, D).contiguous() for x in (q, k, v))
-    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"w8_late_spike_c{int(causal)}")
+    q, k, v = (x.expand(B, H, T, D).contiguous() for x in (q, k, v))
+    check_full(gpu_lib, q, k, v, causal, 0.125, "bf16", f"{kernel}_late_spike_c{int(causal)}")
 
 
-def test_eight_wave_lse_optional(gpu_lib):
-    assert_eight_wave(gpu_lib, 2, 64, 300, True, "bf16")
-    q, k, v = make_qkv(2, 64, 300, D, "bf16", 2400)
+@pytest.mark.parametrize("case", CAUSAL_PAIR, ids=lambda c: c[0])
+def test_eight_wave_lse_optional(gpu_lib, case):
+    kernel, (B, H, T) = case
+    assert_kernel(gpu_lib, kernel, B, H, T, True, "bf16")
+    q, k, v = make_qkv(B, H, T, D, "bf16", 2400)
     qd, kd, vd = (x.to(DEV) for x in (q, k, v))
     o1 = torch.empty_like(qd)
     gpu_lib.attn_fwd_stream(qd, kd, vd, o1, None, True, 0.125)

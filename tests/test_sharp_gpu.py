@@ -1,9 +1,9 @@
 """GPU parity under sharp softmaxes: scales 2 and 16 on N(0, 1) inputs, so a
 row's scores span hundreds of log2 units, most weights underflow to 0 and
 the row maximum keeps jumping by more than the lazy reference's 2^8 bound
-from tile to tile. Every 16-bit entry point (the eight-wave and 128-row
-forward kernels, head dimensions 32 and 128, decode, and both backward
-paths) against the double oracle on the same rounded inputs.
+from tile to tile. Every 16-bit entry point (the eight-wave, key-split and
+128-row forward kernels, head dimensions 32 and 128, decode, and both
+backward paths) against the double oracle on the same rounded inputs.
 
 Tolerances are the 16-bit bounds of the other GPU tests: 2e-2 on O and lse
 (forward, decode) and 2e-2 max(1, max|g|) per gradient. Scores stay float32
@@ -41,18 +41,20 @@ def kernel_of(lib, B, H, T, D, causal, dtype):
     return lib.attn_kernel_name(lib.attn_fused_kernel(B, H, T, D, causal, code))
 
 
-# (B, H, T, D, the kernel that call runs)
-FWD = [(2, 64, 300, 64, "fused_fwd16w8"),   # 384 workgroups of 256 rows
-       (2, 3, 1000, 64, "fused_fwd16<"),     # the 128-row kernel
-       (2, 3, 300, 32, "fused_hd16"),
-       (2, 3, 300, 128, "fused_hd16")]
+# (B, H, T, D, the kernel a causal call runs, the kernel a full call runs)
+FWD = [(4, 64, 300, 64, "fused_fwd16w8<", "fused_fwd16w8<"),   # 256-row workgroups
+       (2, 3, 1000, 64, "fused_fwd16w8s<", "fused_fwd16w8s<"),  # the key split
+       (4, 12, 1024, 64, "fused_fwd16w8s<", "fused_fwd16<"),    # full: the 128-row kernel
+       (2, 3, 300, 32, "fused_hd16", "fused_hd16"),
+       (2, 3, 300, 128, "fused_hd16", "fused_hd16")]
 
 
 @pytest.mark.parametrize("scale", SCALES)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("case", FWD, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_d{c[3]}")
 def test_sharp_forward(gpu_lib, case, causal, scale):
-    B, H, T, D, kernel = case
+    B, H, T, D, k_causal, k_full = case
+    kernel = k_causal if causal else k_full
     assert kernel_of(gpu_lib, B, H, T, D, causal, "bf16").startswith(kernel)
     q, k, v = make_qkv(B, H, T, D, "bf16", 7100 + T + D)
     flush_print(f"[gpu] sharp forward {B}x{H}x{T} D={D} causal={causal} scale={scale}")
