@@ -464,6 +464,25 @@ def test_long_context_sampled(gpu_lib, name):
     check_sampled(gpu_lib, name, 4096, 5001)
 
 
+@pytest.mark.parametrize("shape", [(1, 4, 16384, True), (1, 2, 16384, False), (1, 1, 8191, True)],
+                         ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}_c{int(s[3])}")
+def test_key_split_long_rows_sampled(gpu_lib, shape):
+    """The key split at long rows (few heads: 128 key tiles per group on the
+    longest query tiles, ragged at 8191) on sampled rows, boundaries of the
+    128-row tiles and the last rows included."""
+    B, H, T, causal = shape
+    assert_kernel(gpu_lib, "w8s", B, H, T, causal, "bf16")
+    q, k, v = make_qkv(B, H, T, D, "bf16", 5200 + H + T)
+    flush_print(f"[gpu] key split {B}x{H}x{T} causal={causal}")
+    o, lse = fused(gpu_lib, q, k, v, causal, 0.125)
+    rows = sample_rows(B, H, T, 2048, 5300 + T, boundaries=(128, 256, T // 2))
+    ro, rl = oracle.attention(q, k, v, causal, 0.125, rows=rows)
+    b = tol("bf16", T)
+    assert_close("split O", o.reshape(-1, D).numpy()[rows], ro, b)
+    assert_close("split lse", lse.reshape(-1).numpy()[rows], rl, b)
+    assert np.all(np.isfinite(o.numpy()))
+
+
 @pytest.mark.timeout(600)
 def test_metric_workload_every_row(gpu_lib):
     """All 393216 rows of the 4 x 12 x 8192 bf16 causal workload, in chunks
