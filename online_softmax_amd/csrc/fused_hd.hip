@@ -96,10 +96,16 @@ __device__ inline void hd_sched_skewed() {
     }
 }
 
+// Waves per SIMD the kernel is compiled for: D = 32 fits five (96 VGPRs,
+// no spills; the causal kernel compiled for two took 97, four per SIMD, and
+// ran 4-5% slower at 4 x 12 x 8192; six spill), D = 128 two.
+template <int D>
+constexpr int hd_waves_per_simd() { return D == 32 ? 5 : 2; }
+
 // One workgroup: query tile qt (128 rows) of slice bh. c = |scale| log2(e);
 // qsign negates Q for a negative scale.
 template <int DT, bool CAUSAL, int D>
-__global__ __launch_bounds__(kThreads, 2) void fused_hd16(
+__global__ __launch_bounds__(kThreads, hd_waves_per_simd<D>()) void fused_hd16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     float* __restrict__ lse, int T, int nq, float c, uint32_t qsign) {
