@@ -403,6 +403,28 @@ def decode_leg(osa, torch, oracle, B=4, H=12, Tq=1, Tk=8192, D=64, dtype="bf16",
     log(f"decode D={D}: {mean * 1e3:.1f} us per call back to back (per-call median "
         f"{med * 1e3:.1f}), {achieved:.0f} GB/s = {100 * achieved / PEAK_HBM_GBS:.1f}% of "
         f"{PEAK_HBM_GBS:.0f} GB/s")
+    # the same calls from a HIP graph (a serving loop without per-launch host
+    # work): `copies` calls, one per cache, captured once and replayed
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for k, v in kv:
+            osa.attn_decode_stream(qd, k, v, o, lse, ws, True, scale)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for k, v in kv:
+            osa.attn_decode_stream(qd, k, v, o, lse, ws, True, scale)
+    torch.cuda.synchronize()
+    reps = max(1, steps // copies)
+    rg = time_steps(torch, graph.replay, stream, reps)
+    g_us = rg["mean"] / copies * 1e3
+    out["graph_replay_us_per_call"] = g_us
+    out["graph_replay_GBs"] = algo / (g_us * 1e-6) / 1e9
+    log(f"decode D={D} from a HIP graph: {g_us:.1f} us per call, "
+        f"{algo / (g_us * 1e-6) / 1e9:.0f} GB/s")
+    del graph
     # the same calls through the entry point that allocates nothing (one
     # launch: the last workgroup of each tile merges the split partials),
     # checked against the workspace entry point's output first
@@ -1004,6 +1026,8 @@ def main():
             {p: m["held_beyond_inputs_B"] for p, m in mem.items()},
         "legs": {"bwd": leg(bwd), "bwd_atomic": leg(bwd_atomic), "decode": leg(dec),
                  "decode_noalloc": leg((dec or {}).get("noalloc")),
+                 "decode_graph": None if not dec or "graph_replay_GBs" not in dec else
+                     [dec["graph_replay_GBs"], "GB/s", dec["graph_replay_GBs"] / PEAK_HBM_GBS],
                  "decode_d128": leg(dec128),
                  "d32": leg((hds or {}).get("32")), "d128": leg((hds or {}).get("128")),
                  "recurrence": leg((recur or {}).get("throughput"))},
