@@ -713,15 +713,16 @@ def forward_case(osa, torch, oracle, B, H, T, dtype, seed, steps, warmup,
 
 
 def context_leg(osa, torch, w, qd, kd, vd, steps=20):
-    """Two other programs on the same chip, for context (neither is part of
-    the path): torch's own fused attention (scaled_dot_product_attention,
+    """Other programs on the same chip, for context (none is part of the
+    path): torch's own fused attention (scaled_dot_product_attention,
     flash backend only, on the metric's inputs: the comparison the page
     "Flash attention in PyTorch, then in Triton" draws in section "A kernel
     in Triton"), and the vendor library's dense bf16 matrix product
     (torch.matmul, 8192^3, seeded N(0,1) operands), the matrix-core rate a
-    plain GEMM reaches here. Only the flash backend is allowed: if it cannot
-    run the call, the leg records why instead of falling back to the math
-    path."""
+    plain GEMM reaches here, and a device copy of the decode leg's 100 MB
+    (the rate plain streaming of those bytes reaches here). Only the flash
+    backend is allowed: if it cannot run the call, the leg records why
+    instead of falling back to the math path."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     stream = torch.cuda.current_stream()
     out = {}
@@ -748,11 +749,30 @@ def context_leg(osa, torch, w, qd, kd, vd, steps=20):
     r = timed_calls(torch, lambda: torch.matmul(a, b), stream, steps)
     out["gemm_bf16_8192"] = {"ms": r["mean"], "tflops": 2 * n**3 / (r["mean"] * 1e-3) / 1e12}
     del a, b
+    # what streaming reaches here at the decode leg's size: a device copy
+    # (torch copy_) of 100,663,296 B (the K and V of the 4 x 12 x 8192 x 64
+    # bf16 cache), rotating over four source/destination pairs (800 MB, past
+    # the 256 MB Infinity Cache); bytes read plus bytes written per time
+    nbytes = 2 * 4 * 12 * 8192 * 64 * 2
+    srcs = [torch.ones(nbytes, dtype=torch.uint8, device=qd.device) for _ in range(4)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    turn = [0]
+
+    def copy():
+        i = turn[0] % 4
+        turn[0] += 1
+        dsts[i].copy_(srcs[i])
+    r = timed_calls(torch, copy, stream, 4 * steps)
+    out["hbm_copy_100MB"] = {"us": r["mean"] * 1e3,
+                             "GBs_read_plus_write": 2 * nbytes / (r["mean"] * 1e-3) / 1e9}
+    del srcs, dsts
     torch.cuda.synchronize()
     s = out["torch_sdpa"]
     log("context: torch SDPA (flash) " + (f"{s['ms']:.4f} ms, {s['tflops']:.1f} TFLOP/s"
                                            if "ms" in s else s["error"])
-        + f"; bf16 GEMM 8192^3 {out['gemm_bf16_8192']['tflops']:.1f} TFLOP/s")
+        + f"; bf16 GEMM 8192^3 {out['gemm_bf16_8192']['tflops']:.1f} TFLOP/s"
+        + f"; device copy of 100 MB {out['hbm_copy_100MB']['us']:.1f} us "
+          f"({out['hbm_copy_100MB']['GBs_read_plus_write']:.0f} GB/s read + write)")
     return out
 
 
@@ -1033,7 +1053,8 @@ def main():
                  "recurrence": leg((recur or {}).get("throughput"))},
         "context_tflops": None if ctx is None else
             {"torch_sdpa_flash": ctx["torch_sdpa"].get("tflops"),
-             "gemm_bf16_8192": ctx["gemm_bf16_8192"]["tflops"]},
+             "gemm_bf16_8192": ctx["gemm_bf16_8192"]["tflops"],
+             "hbm_copy_100MB_GBs": ctx["hbm_copy_100MB"]["GBs_read_plus_write"]},
     }
     sys.stderr.flush()
     print(json.dumps(compact(line), separators=(",", ":")), flush=True)
