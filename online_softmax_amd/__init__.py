@@ -17,4 +17,4 @@ from .binding import (  # noqa: F401
     attn_kernel_name, attn_last_hip_error, attn_naive_fwd,
     attn_naive_workspace_bytes, attn_status_string, attn_traffic_bytes,
     dtype_code, load, attn_gated_recurrence_stream, attn_gated_recurrence_flops,
-    gated_recurrence)
+    flash_attention, gated_recurrence)

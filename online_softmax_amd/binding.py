@@ -426,6 +426,62 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = True,
     return dq, dk, dv
 
 
+_FLASH_FN = None
+
+
+def _flash_function():
+    """The autograd Function pairing attn_fwd_stream with the backward entry
+    points, made once (torch is imported lazily, as everywhere here)."""
+    global _FLASH_FN
+    if _FLASH_FN is not None:
+        return _FLASH_FN
+    import torch
+
+    class FlashAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale, atomic):
+            q, k, v = (x.contiguous() for x in (q, k, v))
+            o, lse = attention(q, k, v, causal, scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale, ctx.atomic = causal, scale, atomic
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            if q.dtype not in (torch.bfloat16, torch.float16):
+                raise AttnError(ATTN_ERR_UNSUPPORTED,
+                                "flash_attention backward: the backward pass takes bf16 or f16 "
+                                f"inputs, not {q.dtype}")
+            dq, dk, dv = attention_backward(q, k, v, o, lse, dout.contiguous(), ctx.causal,
+                                            ctx.scale, atomic=ctx.atomic)
+            return dq, dk, dv, None, None, None
+
+    _FLASH_FN = FlashAttention
+    return _FLASH_FN
+
+
+def flash_attention(q, k, v, causal: bool = True, scale: float | None = None,
+                    atomic: bool = False):
+    """O = softmax(Q K^T * scale + causal mask) V for q, k, v [B, H, T, D] as
+    a torch autograd function: the user-facing call of "Flash attention in
+    PyTorch, then in Triton" (section "Backwards, and training with it"),
+    whose forward saves q, k, v, O and the log-sum-exps and whose backward
+    recomputes the probabilities from them. Both passes run this library's
+    kernels (the backward: the two-kernel split, or with atomic=True the
+    single kernel summing dQ with atomics). Under autocast q, k and v are
+    first cast to autocast's dtype, as that page's function does (rotary
+    embeddings leave q and k in float32 while v is bf16). Inputs are made
+    contiguous. scale defaults to 1/sqrt(D)."""
+    import torch
+    if torch.is_autocast_enabled(q.device.type):
+        dt = torch.get_autocast_dtype(q.device.type)
+        q, k, v = (x.to(dt) for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(int(q.shape[-1]))
+    return _flash_function().apply(q, k, v, bool(causal), float(scale), bool(atomic))
+
+
 def attention_decode(q, k, v, causal: bool = True, scale: float | None = None,
                      stream=None):
     """Allocate o, lse and the workspace with torch and run the decode path.
