@@ -724,6 +724,7 @@ def context_leg(osa, torch, w, qd, kd, vd, steps=20):
     backend is allowed: if it cannot run the call, the leg records why
     instead of falling back to the math path."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
+    from online_softmax_amd.inputs import make_qkv
     stream = torch.cuda.current_stream()
     out = {}
     flops = osa.attn_flops(w.B, w.H, w.T, w.D, w.causal)
@@ -742,6 +743,40 @@ def context_leg(osa, torch, w, qd, kd, vd, steps=20):
         del ref, o, lse
     except RuntimeError as e:
         out["torch_sdpa"] = {"error": str(e)[:200]}
+    # forward + backward, the pair the page times for training (its flop
+    # count: the forward's two products and the backward's five, 3.5 times
+    # the forward's): ours through the entry points, torch's through its
+    # flash backend and autograd
+    (dout,) = make_qkv(w.B, w.H, w.T, w.D, w.dtype, 4243)[:1]
+    dd = dout.to(qd.device)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=qd.device)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(osa.attn_bwd_workspace_bytes(w.B, w.H, w.T), dtype=torch.uint8,
+                     device=qd.device)
+
+    def ours_pair():
+        osa.attn_fwd_stream(qd, kd, vd, o, lse, w.causal, w.scale, stream)
+        osa.attn_bwd_stream(qd, kd, vd, o, dd, lse, dq, dk, dv, ws, w.causal, w.scale, stream)
+    r = timed_calls(torch, ours_pair, stream, steps)
+    pair_flops = 3.5 * flops
+    out["fwd_bwd_ours"] = {"ms": r["mean"], "tflops": pair_flops / (r["mean"] * 1e-3) / 1e12}
+    del o, lse, dq, dk, dv, ws
+    try:
+        qg, kg, vg = (x.detach().clone().requires_grad_() for x in (qd, kd, vd))
+
+        def torch_pair():
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                oo = torch.nn.functional.scaled_dot_product_attention(
+                    qg, kg, vg, is_causal=w.causal, scale=w.scale)
+            torch.autograd.grad(oo, (qg, kg, vg), dd)
+        r = timed_calls(torch, torch_pair, stream, steps)
+        out["fwd_bwd_torch_sdpa"] = {"ms": r["mean"],
+                                     "tflops": pair_flops / (r["mean"] * 1e-3) / 1e12}
+        del qg, kg, vg
+    except RuntimeError as e:
+        out["fwd_bwd_torch_sdpa"] = {"error": str(e)[:200]}
+    del dd
     n = 8192
     g = torch.Generator(device="cpu").manual_seed(4242)
     a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(qd.device)
@@ -768,6 +803,10 @@ def context_leg(osa, torch, w, qd, kd, vd, steps=20):
     del srcs, dsts
     torch.cuda.synchronize()
     s = out["torch_sdpa"]
+    fb, tb = out["fwd_bwd_ours"], out["fwd_bwd_torch_sdpa"]
+    log(f"context: forward + backward: ours {fb['ms']:.3f} ms ({fb['tflops']:.1f} TFLOP/s by "
+        "the page's 3.5x count), torch SDPA (flash) "
+        + (f"{tb['ms']:.3f} ms ({tb['tflops']:.1f})" if "ms" in tb else tb["error"]))
     log("context: torch SDPA (flash) " + (f"{s['ms']:.4f} ms, {s['tflops']:.1f} TFLOP/s"
                                            if "ms" in s else s["error"])
         + f"; bf16 GEMM 8192^3 {out['gemm_bf16_8192']['tflops']:.1f} TFLOP/s"
@@ -1053,6 +1092,8 @@ def main():
                  "recurrence": leg((recur or {}).get("throughput"))},
         "context_tflops": None if ctx is None else
             {"torch_sdpa_flash": ctx["torch_sdpa"].get("tflops"),
+             "fwd_bwd_ours": ctx["fwd_bwd_ours"]["tflops"],
+             "fwd_bwd_torch_sdpa_flash": ctx["fwd_bwd_torch_sdpa"].get("tflops"),
              "gemm_bf16_8192": ctx["gemm_bf16_8192"]["tflops"],
              "hbm_copy_100MB_GBs": ctx["hbm_copy_100MB"]["GBs_read_plus_write"]},
     }
