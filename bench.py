@@ -852,6 +852,26 @@ def memory_contrast(osa, torch, w):
         del q, k, v, o, lse
         if path == "naive":
             del ws
+    # forward + backward through flash_attention (the training pair the page
+    # measures memory for): what autograd and the library hold beyond the
+    # inputs and the output gradient (O, lse, dQ, dK, dV, the backward's
+    # workspace of two floats per row)
+    shape = (w.B, w.H, w.T, w.D)
+    q, k, v = (torch.randn(shape, device=dev, dtype=torch.float32).to(torch.bfloat16)
+               .requires_grad_() for _ in range(3))
+    dout = torch.randn(shape, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    grads = torch.autograd.grad(osa.flash_attention(q, k, v, True, w.scale), (q, k, v), dout)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    out["fused_fwd_bwd"] = {"dtype": "bf16", "inputs_B": base,
+                            "held_beyond_inputs_B": peak - base}
+    log(f"memory, fused forward + backward at B={w.B} H={w.H} T={w.T}: held beyond the "
+        f"inputs and dO {(peak - base) / 2**20:.1f} MiB")
+    del q, k, v, dout, grads
     torch.cuda.empty_cache()
     return out
 
