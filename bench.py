@@ -904,8 +904,8 @@ def main():
     ap.add_argument("--no-contrast", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sequence-length sweep and the long context")
-    ap.add_argument("--long-131k", action="store_true",
-                    help="also time the 131072-token long-context case")
+    ap.add_argument("--no-131k", action="store_true",
+                    help="skip the 131072-token long-context case (1 x 16 heads)")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the fused/naive device-memory contrast")
     ap.add_argument("--no-backward", action="store_true",
@@ -1001,7 +1001,7 @@ def main():
                                          label="sweep")
         long_ctx = {}
         for name in ("long_b1h16_t32768_bf16",) + (("long_b1h16_t131072_bf16",)
-                                                   if a.long_131k else ()):
+                                                   if not a.no_131k else ()):
             lw = WORKLOADS[name]
             long_ctx[str(lw.T)] = forward_case(
                 osa, torch, oracle, lw.B, lw.H, lw.T, lw.dtype, lw.seed,
