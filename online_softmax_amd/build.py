@@ -12,6 +12,7 @@ import argparse
 import os
 import shutil
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,13 +40,26 @@ def flags() -> list:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libattn.so; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object (in parallel) and link libattn.so;
+    returns its path."""
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), "-shared", "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    with tempfile.TemporaryDirectory(prefix="attn_build_") as objdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            cmd = [hipcc(), *flags(), "-c", "-o", obj,
+                   os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            objs.append(obj)
+            procs.append((src, subprocess.Popen(cmd)))
+        failed = [src for src, p in procs if p.wait() != 0]
+        if failed:
+            raise RuntimeError("hipcc failed on " + ", ".join(failed))
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-fPIC", "-shared", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 
